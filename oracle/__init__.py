@@ -1,0 +1,211 @@
+"""CPU oracle for the ragged-M grouped GEMM -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package. The HIP library never uses it, and it
+never uses the HIP library: the two share nothing but the seeded input
+generators in ``workloads``.
+
+Contents
+--------
+* ``grouped_gemm`` / ``grouped_gemm_entries``: the fp64 product, from the C
+  file ``oracle.c`` (plain triple loop, one expert at a time). Definition:
+  "Grouped GEMM for Imbalanced Experts on Blackwell: A WIP Worklog", section
+  "What I am measuring" and section 2; InferenceX glossary "Grouped GEMM",
+  "Technical definition".
+* ``tile_list``: the flat, expert-major tile descriptor list of the same
+  worklog, section 2 (the descriptor holds expert, first row, valid rows and
+  first column; tiles stop at expert boundaries; experts with no rows give no
+  tiles). Written here as the plain nested loop over experts, M tiles, N tiles.
+* ``eta``: tile efficiency of section 2.1 -- the share of scheduled rows that
+  hold routed rows. The printed formula did not survive extraction; the
+  reading taken is valid rows over scheduled rows, sum_e m_e / (BM * sum_e
+  ceil(m_e/BM)), which reproduces the printed waste figures (10.2% at BM=64,
+  22.0% at BM=128, skew 1.2, 16k rows) and the 50%/75% padding at 2,048
+  uniform rows.
+* ``eta_estimate``: the section-2.1 skew estimate, balanced throughput times
+  eta (also lost in extraction; pinned by the printed 343.3 and 110.0).
+* ``useful_flops`` / ``algorithmic_bytes``: the worklog's useful-work count
+  (section 1: 2*M_tot*K*N) and the compulsory byte count of section 2.1
+  (A once, B once per expert that has rows, C once).
+* ``adaptive_bm``: the per-expert tile-height rule of the HIP path, written
+  from its stated definition (see the function).
+
+Every function is pinned by ``tests/test_oracle.py`` (brute force, library
+products, closed forms, the pages' printed figures); none is unpinned.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c with gcc (-O2, no fast-math, OpenMP)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+                               "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=False)
+        lib = ctypes.CDLL(_LIB)
+        p = ctypes.c_void_p
+        i32 = ctypes.c_int
+        lib.oracle_grouped_gemm.argtypes = [p, p, p, i32, i32, i32, i32, p, p, p]
+        lib.oracle_grouped_gemm.restype = i32
+        lib.oracle_grouped_gemm_entries.argtypes = [p, p, p, i32, i32, i32, i32, p, p,
+                                                    ctypes.c_int64, p, p]
+        lib.oracle_grouped_gemm_entries.restype = i32
+        lib.oracle_threads.argtypes = []
+        lib.oracle_threads.restype = i32
+        _lib = lib
+    return _lib
+
+
+def threads() -> int:
+    """OpenMP threads the oracle runs on."""
+    return int(_load().oracle_threads())
+
+
+def _ptr(a: np.ndarray):
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+def grouped_gemm(A, B, offsets, M_cap=None, C=None, S=None, want_s=True):
+    """fp64 grouped product. A uint16 [M_cap,K], B uint16 [E,K,N], offsets int32 [E+1].
+
+    Returns (C, S, madds). C and S are float64 [M_cap, N]; rows outside every
+    group keep whatever C/S held on entry (NaN when allocated here).
+    """
+    A = np.ascontiguousarray(A, dtype=np.uint16)
+    B = np.ascontiguousarray(B, dtype=np.uint16)
+    off = np.ascontiguousarray(offsets, dtype=np.int32)
+    E, K, N = B.shape
+    if M_cap is None:
+        M_cap = A.shape[0]
+    assert A.shape == (M_cap, K) and off.shape == (E + 1,)
+    if C is None:
+        C = np.full((M_cap, N), np.nan)
+    if want_s and S is None:
+        S = np.full((M_cap, N), np.nan)
+    madds = ctypes.c_int64(0)
+    rc = _load().oracle_grouped_gemm(_ptr(A), _ptr(B), _ptr(off), E, K, N, M_cap, _ptr(C),
+                                     _ptr(S) if want_s else None, ctypes.byref(madds))
+    if rc != 0:
+        raise ValueError("oracle: malformed problem (offsets or sizes)")
+    return C, S, int(madds.value)
+
+
+def grouped_gemm_entries(A, B, offsets, rows, cols):
+    """C and S at selected (row, col) pairs, one fp64 dot product each."""
+    A = np.ascontiguousarray(A, dtype=np.uint16)
+    B = np.ascontiguousarray(B, dtype=np.uint16)
+    off = np.ascontiguousarray(offsets, dtype=np.int32)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    cols = np.ascontiguousarray(cols, dtype=np.int64)
+    E, K, N = B.shape
+    n = rows.shape[0]
+    c = np.empty(n)
+    s = np.empty(n)
+    rc = _load().oracle_grouped_gemm_entries(_ptr(A), _ptr(B), _ptr(off), E, K, N, A.shape[0],
+                                             _ptr(rows), _ptr(cols), n, _ptr(c), _ptr(s))
+    if rc != 0:
+        raise ValueError("oracle: malformed problem (offsets or sizes)")
+    return c, s
+
+
+def _cdiv(a: int, b: int) -> int:
+    return -(-a // b)
+
+
+def tile_list(offsets, N: int, bm, bn):
+    """Expert-major flat tile list: [(expert, row0, rows, col0), ...].
+
+    bm, bn: one tile height / width for all experts, or a sequence with one
+    entry per expert. Order: expert, then M tile, then N tile innermost.
+    """
+    off = [int(x) for x in offsets]
+    E = len(off) - 1
+    bms = [int(bm)] * E if np.isscalar(bm) else [int(x) for x in bm]
+    bns = [int(bn)] * E if np.isscalar(bn) else [int(x) for x in bn]
+    tiles = []
+    for e in range(E):
+        m_e = off[e + 1] - off[e]
+        BM, BN = bms[e], bns[e]
+        for mt in range(_cdiv(m_e, BM)):
+            for nt in range(_cdiv(N, BN)):
+                tiles.append((e, off[e] + mt * BM, min(BM, m_e - mt * BM), nt * BN))
+    return tiles
+
+
+def eta(sizes, bm) -> float:
+    """Valid rows over scheduled rows for tile height bm (scalar or per expert)."""
+    sizes = [int(x) for x in sizes]
+    bms = [int(bm)] * len(sizes) if np.isscalar(bm) else [int(x) for x in bm]
+    sched = sum(b * _cdiv(m, b) for m, b in zip(sizes, bms))
+    valid = sum(sizes)
+    return valid / sched if sched else 1.0
+
+
+def eta_estimate(balanced_rate: float, eta_value: float) -> float:
+    """Skewed-run throughput estimated from a balanced run: rate * eta."""
+    return balanced_rate * eta_value
+
+
+def useful_flops(m_tot: int, K: int, N: int) -> int:
+    return 2 * int(m_tot) * int(K) * int(N)
+
+
+def algorithmic_bytes(sizes, K: int, N: int, c_bytes: int = 4, in_bytes: int = 2) -> int:
+    """Compulsory bytes: A once, B once per expert with rows, C once."""
+    sizes = [int(x) for x in sizes]
+    m_tot = sum(sizes)
+    active = sum(1 for m in sizes if m > 0)
+    return in_bytes * m_tot * K + in_bytes * K * N * active + c_bytes * m_tot * N
+
+
+# Tile heights the HIP path supports, smallest first.
+BM_CHOICES = (16, 32, 64, 128)
+
+
+def adaptive_bm(sizes, choices=BM_CHOICES):
+    """Per-expert tile height, as the HIP path defines it.
+
+    For each expert the rule takes the height that minimises the cost
+        ceil(m_e / BM) * (BM + H)
+    where H = 64 rows stands for the fixed per-tile work that does not grow
+    with the tile height (streaming the expert's weight slice through the
+    tile, the barriers and the epilogue set-up). Ties go to the larger
+    height. An expert with no rows gets the smallest height (and no tiles).
+    The worklog (sections 2.1, 6 and 7) motivates the trade -- padding falls
+    with BM while per-tile staging work rises -- and proposes choosing BM
+    from the expert sizes; the constant H is this implementation's own.
+    """
+    H = 64
+    out = []
+    for m in (int(x) for x in sizes):
+        if m <= 0:
+            out.append(choices[0])
+            continue
+        best, best_cost = None, None
+        for b in choices:
+            cost = _cdiv(m, b) * (b + H)
+            if best_cost is None or cost <= best_cost:
+                best, best_cost = b, cost
+        out.append(best)
+    return out

@@ -1,0 +1,278 @@
+"""Pins for the CPU oracle (no GPU).
+
+Each test checks the oracle against something other than itself: a scalar
+brute force written from the textbook definition, numpy's float64 matrix
+product (a library routine), closed forms (identity and permutation weights,
+the multiply-add count) and the figures the worklog prints (tests/golden).
+A dropped term, a wrong index, a transposed operand or a wrong expert slice
+in the oracle fails at least one of them.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "page_figures.json")
+
+
+def _decode(bits):
+    return wl.bf16_bits_to_f32(bits).astype(np.float64)
+
+
+def _py_brute(A, B, off):
+    """Scalar triple loop from the definition, pure Python floats, no numpy math."""
+    E, K, N = B.shape
+    Af = _decode(A).tolist()
+    Bf = _decode(B).tolist()
+    out = {}
+    for e in range(E):
+        for i in range(int(off[e]), int(off[e + 1])):
+            for j in range(N):
+                acc = 0.0
+                for k in range(K):
+                    acc += Af[i][k] * Bf[e][k][j]
+                out[(i, j)] = acc
+    return out
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2, 3])
+def test_brute_force_integer_inputs(seed):
+    rng = np.random.default_rng(100 + seed)
+    E = int(rng.integers(1, 4))
+    K = int(rng.integers(1, 9))
+    N = int(rng.integers(1, 9))
+    sizes = rng.integers(0, 6, size=E)
+    w = wl.make_workload(E=E, K=K, N=N, sizes=sizes, seed=seed, values="int", M_cap=int(sizes.sum()) + 2)
+    C, S, madds = oracle.grouped_gemm(w.A, w.B, w.offsets)
+    ref = _py_brute(w.A, w.B, w.offsets)
+    for (i, j), v in ref.items():
+        assert C[i, j] == v  # integers below 2^24: exact in any order
+    # rows outside every group untouched
+    assert np.isnan(C[w.M_tot:]).all()
+    assert madds == int(sizes.sum()) * K * N
+
+
+@pytest.mark.parametrize("name", ["tiny"])
+def test_tiny_against_python_brute_force(name):
+    w = wl.make_workload(name)
+    C, _, _ = oracle.grouped_gemm(w.A, w.B, w.offsets)
+    ref = _py_brute(w.A[:, :64], w.B[:, :64, :8], w.offsets)  # K,N cut for speed
+    Cc, _, _ = oracle.grouped_gemm(np.ascontiguousarray(w.A[:, :64]), np.ascontiguousarray(w.B[:, :64, :8]), w.offsets)
+    for (i, j), v in ref.items():
+        assert Cc[i, j] == pytest.approx(v, rel=1e-15, abs=1e-300)
+    assert np.isfinite(C).all()
+
+
+def _numpy_per_expert(w):
+    Af = _decode(w.A)
+    Bf = _decode(w.B)
+    out = np.full((w.M_cap, w.N), np.nan)
+    sab = np.full((w.M_cap, w.N), np.nan)
+    for e in range(w.E):
+        r0, r1 = int(w.offsets[e]), int(w.offsets[e + 1])
+        out[r0:r1] = Af[r0:r1] @ Bf[e]
+        sab[r0:r1] = np.abs(Af[r0:r1]) @ np.abs(Bf[e])
+    return out, sab
+
+
+@pytest.mark.parametrize("case", [
+    dict(name="tiny"),
+    dict(E=5, K=96, N=40, sizes=[7, 0, 33, 1, 12], seed=11),
+    dict(E=3, K=200, N=24, sizes=[0, 50, 0], seed=12),
+    dict(E=1, K=64, N=64, sizes=[65], seed=13),
+])
+def test_equals_separate_dense_products(case):
+    w = wl.make_workload(case.pop("name")) if "name" in case else wl.make_workload(**case)
+    C, S, _ = oracle.grouped_gemm(w.A, w.B, w.offsets)
+    ref, sref = _numpy_per_expert(w)
+    m = w.M_tot
+    # different summation orders of the same fp64 sum: |diff| <= K * 2^-53 * S
+    bound = w.K * 2.0 ** -53 * sref[:m] + 1e-300
+    assert (np.abs(C[:m] - ref[:m]) <= bound).all()
+    assert np.allclose(S[:m], sref[:m], rtol=w.K * 2.0 ** -52, atol=0)
+    assert (S[:m] >= np.abs(C[:m])).all()
+
+
+def test_transposed_or_wrong_expert_is_caught():
+    # the dense-product pin really distinguishes a transposed B or a shifted expert
+    w = wl.make_workload(E=3, K=32, N=32, sizes=[5, 6, 7], seed=21)
+    C, _, _ = oracle.grouped_gemm(w.A, w.B, w.offsets)
+    Bt = np.ascontiguousarray(np.transpose(w.B, (0, 2, 1)))
+    Ct, _, _ = oracle.grouped_gemm(w.A, Bt, w.offsets)
+    assert not np.allclose(C, Ct)
+    Bs = np.ascontiguousarray(np.roll(w.B, 1, axis=0))
+    Cs, _, _ = oracle.grouped_gemm(w.A, Bs, w.offsets)
+    assert not np.allclose(C, Cs)
+
+
+@pytest.mark.parametrize("sizes", [
+    [0, 0, 5, 3], [4, 2, 0, 0], [3, 0, 0, 4], [0, 0, 0, 0], [7], [0], [0, 9, 0],
+])
+def test_empty_groups_write_no_rows(sizes):
+    E = len(sizes)
+    w = wl.make_workload(E=E, K=16, N=24, sizes=sizes, seed=5, M_cap=sum(sizes) + 3)
+    C, S, madds = oracle.grouped_gemm(w.A, w.B, w.offsets)
+    m = w.M_tot
+    assert np.isfinite(C[:m]).all() and np.isfinite(S[:m]).all()
+    assert np.isnan(C[m:]).all() and np.isnan(S[m:]).all()
+    assert madds == m * 16 * 24
+
+
+def test_identity_weights_reproduce_a_exactly():
+    w = wl.make_workload("tiny")
+    eye = wl.f32_to_bf16_bits(np.eye(256, dtype=np.float32))
+    B = np.broadcast_to(eye, (4, 256, 256)).copy()
+    C, _, _ = oracle.grouped_gemm(w.A, B, w.offsets)
+    assert (C == wl.bf16_bits_to_f32(w.A).astype(np.float64)).all()
+
+
+def test_permutation_weights_permute_columns_exactly():
+    w = wl.make_workload("tiny")
+    rng = np.random.default_rng(7)
+    B = np.zeros((4, 256, 256), dtype=np.uint16)
+    perms = []
+    for e in range(4):
+        p = rng.permutation(256)
+        P = np.zeros((256, 256), dtype=np.float32)
+        P[p, np.arange(256)] = 1.0  # column j takes input column p[j]
+        B[e] = wl.f32_to_bf16_bits(P)
+        perms.append(p)
+    C, _, _ = oracle.grouped_gemm(w.A, B, w.offsets)
+    Af = wl.bf16_bits_to_f32(w.A).astype(np.float64)
+    for e in range(4):
+        r0, r1 = int(w.offsets[e]), int(w.offsets[e + 1])
+        assert (C[r0:r1] == Af[r0:r1][:, perms[e]]).all()
+
+
+def test_group_split_invariance_bitwise():
+    w = wl.make_workload(E=2, K=80, N=48, sizes=[20, 9], seed=31)
+    C, S, _ = oracle.grouped_gemm(w.A, w.B, w.offsets)
+    # split expert 0 into rows [0,8) and [8,20), both using B_0
+    off2 = np.array([0, 8, 20, 29], dtype=np.int32)
+    B2 = np.ascontiguousarray(np.stack([w.B[0], w.B[0], w.B[1]]))
+    C2, S2, _ = oracle.grouped_gemm(w.A, B2, off2)
+    assert (C2 == C).all() and (S2 == S).all()
+
+
+def test_flop_count_closed_form():
+    w = wl.make_workload(E=4, K=40, N=8, sizes=[3, 0, 11, 2], seed=3)
+    _, _, madds = oracle.grouped_gemm(w.A, w.B, w.offsets, want_s=False)
+    assert 2 * madds == oracle.useful_flops(16, 40, 8) == 2 * 16 * 40 * 8
+    g = json.load(open(GOLDEN))["useful_work"][0]
+    f = oracle.useful_flops(g["m_tot"], g["K"], g["N"])
+    assert f == 90_194_313_216
+    assert round(f / 1e9, 1) == g["gflop_rounded_1dp"]
+
+
+def test_entries_match_full_and_numpy():
+    w = wl.make_workload(E=3, K=300, N=50, sizes=[10, 0, 25], seed=41)
+    C, S, _ = oracle.grouped_gemm(w.A, w.B, w.offsets)
+    rng = np.random.default_rng(0)
+    rows = rng.integers(0, w.M_tot, size=40)
+    cols = rng.integers(0, w.N, size=40)
+    c, s = oracle.grouped_gemm_entries(w.A, w.B, w.offsets, rows, cols)
+    assert (c == C[rows, cols]).all() and (s == S[rows, cols]).all()
+    Af = _decode(w.A)
+    Bf = _decode(w.B)
+    for t in range(40):
+        e = int(np.searchsorted(w.offsets, rows[t], side="right") - 1)
+        assert c[t] == pytest.approx(float(np.dot(Af[rows[t]], Bf[e][:, cols[t]])), rel=1e-13, abs=1e-15)
+
+
+def test_malformed_offsets_rejected():
+    w = wl.make_workload(E=2, K=8, N=8, sizes=[2, 2], seed=1)
+    for bad in ([1, 2, 4], [0, 3, 2], [0, 2, 9]):
+        with pytest.raises(ValueError):
+            oracle.grouped_gemm(w.A, w.B, np.array(bad, dtype=np.int32))
+
+
+# ---- tile list, eta and byte model against the worklog's printed figures ----
+
+def _golden_sizes(name):
+    if name == "uniform16k":
+        return [256] * 64
+    if name == "skew16k_page":
+        return list(wl.page_skew_sizes(16384, 64, 1.2))
+    if name == "uniform2k":
+        return [32] * 64
+    raise KeyError(name)
+
+
+def test_page_skew_law_figures():
+    for g in json.load(open(GOLDEN))["skew_law"]:
+        s = wl.page_skew_sizes(g["m_tot"], g["experts"], g["s"])
+        assert int(s.sum()) == g["m_tot"]
+        assert int(s.max()) == g["largest"] and int(s.min()) == g["smallest"]
+
+
+def test_tile_counts_from_pages():
+    for g in json.load(open(GOLDEN))["tile_counts"]:
+        sizes = _golden_sizes(g["workload"])
+        off = wl.offsets_from_sizes(sizes)
+        tiles = oracle.tile_list(off, 2688, g["bm"], g["bn"])
+        assert len(tiles) == g["count"], g["cite"]
+
+
+def test_tile_list_structure():
+    off = wl.offsets_from_sizes([3, 0, 17, 9, 0])
+    tiles = oracle.tile_list(off, 256, 16, 128)
+    # expert 1 and 4 empty: no tiles; expert 2 -> 2 M tiles x 2 N tiles
+    assert tiles == [
+        (0, 0, 3, 0), (0, 0, 3, 128),
+        (2, 3, 16, 0), (2, 3, 16, 128), (2, 19, 1, 0), (2, 19, 1, 128),
+        (3, 20, 9, 0), (3, 20, 9, 128),
+    ]
+    # every valid (row, col-block) is covered exactly once, never past the expert
+    cover = {}
+    for e, r0, rows, c0 in oracle.tile_list(off, 200, 16, 64):
+        assert rows >= 1 and r0 >= off[e] and r0 + rows <= off[e + 1]
+        for r in range(r0, r0 + rows):
+            cover[(r, c0)] = cover.get((r, c0), 0) + 1
+    assert set(cover.values()) == {1} and len(cover) == 29 * 4
+
+
+def test_eta_from_pages():
+    for g in json.load(open(GOLDEN))["eta"]:
+        v = oracle.eta(_golden_sizes(g["workload"]), g["bm"])
+        if "waste_pct" in g:
+            assert round(100 * (1 - v), 1) == g["waste_pct"], g["cite"]
+        if "eta" in g:
+            assert round(v, 3) == g["eta"], g["cite"]
+
+
+def test_eta_estimates_from_pages():
+    for g in json.load(open(GOLDEN))["eta_estimates"]:
+        # the page multiplies by eta as it prints it, to three places (0.780, 0.250)
+        v = round(oracle.eta(_golden_sizes(g["workload"]), g["bm"]), 3)
+        assert round(oracle.eta_estimate(g["balanced"], v), 1) == g["estimate"], g["cite"]
+
+
+def test_compulsory_bytes_from_pages():
+    for g in json.load(open(GOLDEN))["compulsory_bytes"]:
+        b = oracle.algorithmic_bytes(_golden_sizes(g["workload"]), 1024, 2688, c_bytes=g["c_bytes"])
+        assert b == 473_956_352
+        assert round(b / 1e6) == g["mb_rounded"]
+    # the fp32-output figure used for this library, and empty experts' B not counted
+    assert oracle.algorithmic_bytes([256] * 64, 1024, 2688) == 562_036_736
+    assert oracle.algorithmic_bytes([3, 0, 17, 9], 256, 256) == (2 * 29 * 256 + 2 * 256 * 256 * 3 + 4 * 29 * 256)
+
+
+def test_adaptive_bm_special_cases():
+    # multiples of the largest height and very small experts are decided by padding alone
+    assert oracle.adaptive_bm([128, 256, 4096]) == [128, 128, 128]
+    assert oracle.adaptive_bm([1, 5, 16]) == [16, 16, 16]
+    assert oracle.adaptive_bm([32]) == [32]
+    assert oracle.adaptive_bm([0]) == [16]
+    # worked by hand: m=48 -> costs 16:3*80=240, 32:2*96=192, 64:1*128=128, 128:192 -> 64
+    assert oracle.adaptive_bm([48]) == [64]
+    # m=130 -> 16:9*80=720, 32:5*96=480, 64:3*128=384, 128:2*192=384 -> tie -> 128
+    assert oracle.adaptive_bm([130]) == [128]
+    # eta never below the uniform-BM=128 eta on the page skew law
+    s = _golden_sizes("skew16k_page")
+    assert oracle.eta(s, oracle.adaptive_bm(s)) >= oracle.eta(s, 128)

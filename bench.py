@@ -1,0 +1,223 @@
+#!/usr/bin/env python3
+"""Throughput of the gfx950 ragged-M grouped GEMM on one MI355X.
+
+One step = one launch of the whole path (device tile schedule, per-expert tile
+height, bf16 matrix-core K loop, register-direct epilogue) over one batch of
+synthetic, seeded inputs already resident in HBM. Default workload: the
+decode shape of a Mixture-of-Experts layer's share on one GPU (32 experts x 16
+routed rows, K=6144, N=4096).
+
+Prints one JSON line:
+  value      useful TFLOP/s = 2*M_tot*K*N / (time per step)
+  roofline   the kernel against its bound: algorithmic bytes (A once, B once
+             per expert with rows, C once as fp32) per launch over the average
+             launch time (HIP events on the launch stream), vs 8 TB/s HBM3E;
+             or useful flops vs 2.5 PFLOP/s dense bf16 when the workload's
+             arithmetic intensity is above the ridge point. "traffic" is the
+             measured HBM bytes per launch from the committed rocprofv3
+             counter summary, when that summary matches the current kernel
+             sources, else null.
+  cpu_baseline  the CPU oracle timed on a bounded sample of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--config decode] [--bm 0]
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "useful TFLOP/s (2*M_tot*K*N/t) + HBM GB/s, % of roofline, 1 MI355X"
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+RIDGE = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)  # flop per byte
+KERNEL_NAME = "grouped_gemm_kernel"
+
+DESCRIPTIONS = {
+    "tiny": "tiny ragged grouped GEMM: E=4, K=256, N=256, m=[3,0,17,9]",
+    "decode": "decode shape: E=32 experts x 16 rows (M_tot=512), K=6144, N=4096",
+    "uniform16k": "uniform large batch: E=64 x 256 rows (M_tot=16384), K=1024, N=2688",
+    "skew16k": "skewed routing rank^-1.2: E=64, M_tot=16384, K=1024, N=2688",
+    "skew2k_wide": "small skewed batch, wide weights: E=32, M_tot=2048 rank^-1.2, K=6144, N=4096",
+    "skew16k_page": "page skew law (e+1)^-1.2: E=64, M_tot=16384, K=1024, N=2688",
+}
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "moe_ragged_grouped_amd", "csrc")
+    for fn in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, fn), "rb") as f:
+            h.update(fn.encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(config, bm):
+    """HBM bytes per launch from the committed counter summary, if still current."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get("%s/bm%d" % (config, bm))
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, budget_s=12.0):
+    """Time the CPU oracle on the first n experts of the workload (bounded sample)."""
+    import numpy as np
+
+    import oracle
+
+    nz = [e for e in range(w.E) if w.sizes[e] > 0]
+
+    def run(n):
+        e1 = nz[n - 1] + 1
+        off = w.offsets[: e1 + 1].copy()
+        rows = int(off[-1])
+        A = w.A[:rows]
+        B = w.B[:e1]
+        t0 = time.perf_counter()
+        oracle.grouped_gemm(A, B, off, M_cap=rows)
+        dt = time.perf_counter() - t0
+        return dt, 2.0 * rows * w.K * w.N, rows, e1
+
+    dt1, _, _, _ = run(1)
+    n = int(max(1, min(len(nz), budget_s / max(dt1, 1e-6))))
+    dt, flops, rows, e1 = run(n)
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": oracle.threads(),
+        "kind": "oracle",
+        "sample": "experts 0..%d of the %s workload (%d routed rows, full K=%d and N=%d), "
+                  "fp64 accumulation plus the sum|ab| bound, %.1f s" % (e1 - 1, w.name, rows, w.K, w.N, dt),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="decode", choices=sorted(DESCRIPTIONS))
+    ap.add_argument("--bm", type=int, default=0, help="0 = per-expert tile height chosen on the device")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 1 GiB device copy (for counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(expert-parallel sharding is described in DESIGN.md); run with --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import moe_ragged_grouped_amd as gg
+    import workloads as wl
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n,
+                          "launches": 5}))
+        return
+
+    print("bench: drawing workload %s" % args.config, file=sys.stderr, flush=True)
+    w = wl.make_workload(args.config)
+    A = torch.from_numpy(w.A.view(np.int16)).to(dev).view(torch.bfloat16)
+    B = torch.from_numpy(w.B.view(np.int16)).to(dev).view(torch.bfloat16)
+    off = torch.from_numpy(w.offsets).to(dev)
+    C = torch.empty((w.M_cap, w.N), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    print("bench: warmup %d launches" % args.warmup, file=sys.stderr, flush=True)
+    gg.grouped_gemm(A, B, off, out=C, bm=args.bm)  # correctness launch position of the protocol
+    for _ in range(args.warmup):
+        gg.grouped_gemm(A, B, off, out=C, bm=args.bm)
+    torch.cuda.synchronize()
+
+    print("bench: timing %d launches" % args.steps, file=sys.stderr, flush=True)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        gg.grouped_gemm(A, B, off, out=C, bm=args.bm)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev_s = ev0.elapsed_time(ev1) / 1e3
+    step_s = max(wall, ev_s) / args.steps      # the step as the host sees it
+    launch_s = ev_s / args.steps                # average launch on the stream
+
+    useful = 2.0 * w.M_tot * w.K * w.N
+    alg_bytes = 2 * w.M_tot * w.K + 2 * w.K * w.N * int((w.sizes > 0).sum()) + 4 * w.M_tot * w.N
+    intensity = useful / alg_bytes
+    hbm_gbs = alg_bytes / launch_s / 1e9
+    tflops_launch = useful / launch_s / 1e12
+    traffic = measured_traffic(args.config, args.bm)
+    if intensity < RIDGE:
+        roof = {"bound": "hbm", "achieved": round(hbm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(hbm_gbs / HBM_PEAK_GBS, 4), "traffic": traffic}
+    else:
+        roof = {"bound": "mfma", "achieved": round(tflops_launch, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(tflops_launch / MFMA_BF16_PEAK_TFLOPS, 4),
+                "traffic": traffic}
+    roof["kernel"] = KERNEL_NAME
+    roof["algorithmic_bytes_per_launch"] = alg_bytes
+    roof["avg_launch_us"] = round(launch_s * 1e6, 2)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(w)
+
+    line = {
+        "metric": METRIC,
+        "value": round(useful / step_s / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_s * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded normal draws rounded to bf16, no dataset)",
+        "config": {"workload": DESCRIPTIONS[args.config], "name": args.config, "E": w.E, "K": w.K,
+                   "N": w.N, "M_tot": w.M_tot, "bm": args.bm or "per-expert", "out_dtype": "fp32"},
+        "hbm_gbs": round(hbm_gbs, 1),
+        "hbm_frac": round(hbm_gbs / HBM_PEAK_GBS, 4),
+        "mfma_frac": round(tflops_launch / MFMA_BF16_PEAK_TFLOPS, 4),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

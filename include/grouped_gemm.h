@@ -1,0 +1,108 @@
+/*
+ * Ragged-M grouped GEMM for AMD Instinct MI355X (gfx950) -- C ABI.
+ *
+ * One call computes E independent bf16 products with fp32 accumulation,
+ *     C[off[e]:off[e+1], :] = A[off[e]:off[e+1], :] x B[e]      for e < E,
+ * where the row count m_e = off[e+1] - off[e] of every group is read on the
+ * device at run time and may be zero or heavily skewed. This is the
+ * expert-FFN projection of a Mixture-of-Experts layer after routing, as
+ * defined by "Grouped GEMM for Imbalanced Experts on Blackwell: A WIP
+ * Worklog" (section "What I am measuring" and section 2, "The Grouped
+ * Problem and the flat tile list") and by the InferenceX glossary entry
+ * "Grouped GEMM" ("Technical definition"): rows arrive grouped by expert,
+ * K and N are fixed, the group sizes are only known at run time, and every
+ * expert's product runs in a single launch.
+ *
+ * Conventions shared by every entry point below:
+ *  - All array pointers are DEVICE pointers owned by the caller; the library
+ *    keeps no reference to them after the call returns and allocates no
+ *    device memory.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream). The
+ *    call only enqueues work on it: no host synchronisation, no device to
+ *    host copy. Results are ready when the stream reaches that point.
+ *  - Errors the host can see (bad sizes, null or misaligned pointers,
+ *    unsupported shapes) return a status and enqueue nothing.
+ *  - Malformed offsets (off[0] != 0, decreasing entries, entries outside
+ *    [0, M_cap]) are the caller's bug; they never make the kernel read or
+ *    write outside A[0:M_cap], B[0:E] and C[0:M_cap]: every offset is clamped
+ *    into [0, M_cap] and a group whose clamped end precedes its clamped start
+ *    is treated as empty.
+ *  - Calls on different streams may run concurrently; the library holds no
+ *    mutable state besides a per-device cache of launch limits.
+ */
+#ifndef MOE_RAGGED_GROUPED_AMD_GROUPED_GEMM_H
+#define MOE_RAGGED_GROUPED_AMD_GROUPED_GEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GG_OK = 0,
+  GG_ERR_INVALID_VALUE = 1, /* null pointer, non-positive size, bad bm        */
+  GG_ERR_MISALIGNED = 2,    /* pointer not 16-byte aligned, K or N not 8k     */
+  GG_ERR_UNSUPPORTED = 3,   /* E > GG_MAX_EXPERTS or index range beyond int32 */
+  GG_ERR_LAUNCH = 4         /* the HIP runtime refused the launch             */
+} gg_status_t;
+
+/* Largest number of groups one call accepts (the per-group tables live in LDS). */
+#define GG_MAX_EXPERTS 1024
+
+/*
+ * gg_grouped_gemm_bf16 -- the grouped product (worklog section 2; glossary
+ * "Technical definition").
+ *
+ *   A   bf16 [M_cap][K], row-major (K fastest). Rows are grouped by expert:
+ *       rows off[e] .. off[e+1]-1 belong to expert e. Rows at or beyond
+ *       off[E] are never read.
+ *   B   bf16 [E][K][N], row-major (N fastest): B[e] is expert e's weight.
+ *       The slice of an expert with no rows is never read.
+ *   group_offsets  int32 [E+1] on the device: 0 = off[0] <= off[1] <= ...
+ *       <= off[E] = M_tot <= M_cap.
+ *   C   fp32 [M_cap][N], row-major. Rows [0, M_tot) are overwritten with the
+ *       product (not accumulated into); rows [M_tot, M_cap) are not touched.
+ *   E in [1, GG_MAX_EXPERTS]; K >= 8 and N >= 8, both multiples of 8;
+ *   M_cap >= 0 (0: nothing is enqueued).
+ *   bm  tile height: 16, 32, 64 or 128 for every expert, or 0 to let the
+ *       device choose per expert from its row count (the trade between
+ *       padding in the last tile and per-tile work that the worklog
+ *       describes in sections 2.1, 6 and 7).
+ *   A, B and C must be 16-byte aligned; group_offsets 4-byte aligned.
+ *
+ * Accumulation is fp32 inside the matrix cores; a result differs from the
+ * exact sum by at most a few units of K * 2^-24 relative to sum_k |a*b|.
+ */
+gg_status_t gg_grouped_gemm_bf16(const void *A, const void *B, const int32_t *group_offsets,
+                                 float *C, int32_t E, int32_t K, int32_t N, int32_t M_cap,
+                                 int32_t bm, void *stream);
+
+/*
+ * gg_tile_schedule -- the flat tile list the product kernel consumes,
+ * written out (worklog section 2: one descriptor per output tile of one
+ * expert, expert-major order, tiles stopping at expert boundaries, empty
+ * experts contributing none).
+ *
+ * The device builds it from group_offsets with exactly the code the product
+ * kernel runs; tile t of the list is written as 5 int32
+ *     tiles[5t .. 5t+4] = { expert, row0, rows, col0, bm }
+ * in tile-id order (expert, then M tile, then N tile innermost). col0 steps
+ * by the tile width of the chosen tile height (128 columns for every height
+ * in this version). At most max_tiles descriptors are written; *n_tiles (a
+ * device int32) receives the full count even when it exceeds max_tiles.
+ * Arguments E, N, M_cap, bm and the offsets rules are those of
+ * gg_grouped_gemm_bf16; tiles may be NULL when max_tiles == 0.
+ */
+gg_status_t gg_tile_schedule(const int32_t *group_offsets, int32_t E, int32_t N, int32_t M_cap,
+                             int32_t bm, int32_t *tiles, int32_t *n_tiles, int32_t max_tiles,
+                             void *stream);
+
+/* Static English text for a status code. */
+const char *gg_status_string(gg_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_RAGGED_GROUPED_AMD_GROUPED_GEMM_H */

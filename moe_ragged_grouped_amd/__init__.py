@@ -1,0 +1,122 @@
+"""Python binding of the gfx950 ragged-M grouped GEMM library.
+
+Argument marshalling only: every step of the computation runs in the HIP
+library (``libmoe_ragged_grouped_amd.so``, built from ``csrc/``). PyTorch
+supplies device memory and the stream. There is no fallback: if the library
+is missing or a call fails, an exception is raised.
+
+    C = grouped_gemm(A, B, offsets)            # A [M_cap,K] bf16, B [E,K,N] bf16,
+                                               # offsets int32 [E+1], C [M_cap,N] fp32
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = ["grouped_gemm", "tile_schedule", "library_path", "load_library", "GroupedGemmError",
+           "BM_CHOICES", "TILE_N", "MAX_EXPERTS", "SYMBOLS"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libmoe_ragged_grouped_amd.so")
+
+BM_CHOICES = (16, 32, 64, 128)
+TILE_N = 128
+MAX_EXPERTS = 1024
+SYMBOLS = ("gg_grouped_gemm_bf16", "gg_tile_schedule", "gg_status_string")
+
+_lib = None
+
+
+class GroupedGemmError(RuntimeError):
+    pass
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise GroupedGemmError(
+                "HIP library %s is not built; run `python -m moe_ragged_grouped_amd.build`" % _LIB_PATH)
+        lib = ctypes.CDLL(_LIB_PATH)
+        vp, i32 = ctypes.c_void_p, ctypes.c_int32
+        lib.gg_grouped_gemm_bf16.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
+        lib.gg_grouped_gemm_bf16.restype = ctypes.c_int
+        lib.gg_tile_schedule.argtypes = [vp, i32, i32, i32, i32, vp, vp, i32, vp]
+        lib.gg_tile_schedule.restype = ctypes.c_int
+        lib.gg_status_string.argtypes = [ctypes.c_int]
+        lib.gg_status_string.restype = ctypes.c_char_p
+        _lib = lib
+    return _lib
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        msg = load_library().gg_status_string(status).decode()
+        raise GroupedGemmError("%s: status %d (%s)" % (what, status, msg))
+
+
+def _stream_handle(device, stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def grouped_gemm(A, B, offsets, out=None, bm: int = 0, stream=None):
+    """C[off[e]:off[e+1]] = A[off[e]:off[e+1]] @ B[e] for every expert e, in one launch.
+
+    A: bf16 [M_cap, K]; B: bf16 [E, K, N]; offsets: int32 [E+1] (device);
+    out: optional fp32 [M_cap, N]; bm: 0 (per-expert choice on the device)
+    or 16/32/64/128. Rows of ``out`` at or past offsets[E] are left as they
+    were. Enqueued on ``stream`` (default: torch's current stream).
+    """
+    import torch
+    lib = load_library()
+    if A.dtype != torch.bfloat16 or B.dtype != torch.bfloat16:
+        raise TypeError("A and B must be bfloat16")
+    if offsets.dtype != torch.int32:
+        raise TypeError("offsets must be int32")
+    if A.dim() != 2 or B.dim() != 3 or offsets.dim() != 1:
+        raise ValueError("shapes: A [M_cap,K], B [E,K,N], offsets [E+1]")
+    if not (A.is_cuda and B.is_cuda and offsets.is_cuda):
+        raise ValueError("A, B and offsets must be device tensors")
+    if not (A.is_contiguous() and B.is_contiguous() and offsets.is_contiguous()):
+        raise ValueError("A, B and offsets must be contiguous")
+    E, K, N = B.shape
+    M_cap = A.shape[0]
+    if A.shape[1] != K or offsets.shape[0] != E + 1:
+        raise ValueError("shape mismatch: A %s, B %s, offsets %s" % (tuple(A.shape), tuple(B.shape),
+                                                                      tuple(offsets.shape)))
+    if out is None:
+        out = torch.empty((M_cap, N), dtype=torch.float32, device=A.device)
+    elif out.dtype != torch.float32 or tuple(out.shape) != (M_cap, N) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous fp32 [M_cap, N] tensor")
+    st = lib.gg_grouped_gemm_bf16(A.data_ptr(), B.data_ptr(), offsets.data_ptr(), out.data_ptr(),
+                                  E, K, N, M_cap, int(bm), _stream_handle(A.device, stream))
+    _check(st, "gg_grouped_gemm_bf16")
+    return out
+
+
+def tile_schedule(offsets, N: int, M_cap: int, bm: int = 0, max_tiles: int = None, stream=None):
+    """The device-built tile list: int32 tensor [n_tiles, 5] of (expert, row0, rows, col0, bm)."""
+    import torch
+    lib = load_library()
+    if offsets.dtype != torch.int32 or not offsets.is_cuda or offsets.dim() != 1:
+        raise TypeError("offsets must be a 1-D int32 device tensor")
+    E = offsets.shape[0] - 1
+    if max_tiles is None:
+        hmin = bm if bm else BM_CHOICES[0]
+        max_tiles = (M_cap // hmin + E) * (-(-N // TILE_N))
+    tiles = torch.empty((max(max_tiles, 1), 5), dtype=torch.int32, device=offsets.device)
+    n = torch.zeros(1, dtype=torch.int32, device=offsets.device)
+    st = lib.gg_tile_schedule(offsets.data_ptr(), E, N, M_cap, int(bm), tiles.data_ptr(), n.data_ptr(),
+                              int(max_tiles), _stream_handle(offsets.device, stream))
+    _check(st, "gg_tile_schedule")
+    count = int(n.item())
+    return tiles[:min(count, max_tiles)], count

@@ -1,0 +1,216 @@
+// Ragged-M grouped GEMM for gfx950: kernels and the C-ABI entry points
+// declared in include/grouped_gemm.h.
+//
+// One persistent launch serves every expert. Each workgroup rebuilds the
+// tile-count prefix from the device-resident group offsets (gg_schedule.h),
+// then walks tile ids with a stride of the grid size, decoding each id into
+// {expert, row0, rows, col0, bm} and running that tile's K loop and epilogue
+// (gg_mainloop.h). The grid is sized from the occupancy of the kernel and the
+// CU count, capped by an upper bound of the tile count that the host can
+// derive from M_cap alone, so the launch never waits on the group sizes.
+//
+// XCD-aware order: MI355X hands consecutive workgroup ids round-robin to its
+// 8 XCDs, each with a private L2. Workgroup b processes, in its i-th round,
+// tile i*G + (b % 8) * (G / 8) + b / 8, so every XCD works on a contiguous
+// run of the expert-major list; tiles that share an expert's A rows (same M
+// tile) or its weight columns (same N tile) then meet in the same L2.
+
+#include "../../include/grouped_gemm.h"
+#include "gg_common.h"
+#include "gg_mainloop.h"
+#include "gg_schedule.h"
+
+#include <mutex>
+
+namespace gg {
+
+constexpr int kXcds = 8;
+
+struct Params {
+  const uint16_t *A;
+  const uint16_t *B;
+  const int32_t *off;
+  float *C;
+  int E, K, N, M_cap;
+  int bm_fixed;  // 0 = per-expert choice
+};
+
+template <class Cfg>
+__device__ __forceinline__ void tile_body(const Params &p, const Tile &t, lds_u16 *lds) {
+  const uint16_t *Be = p.B + (size_t)t.expert * p.K * p.N;
+  run_tile<Cfg>(p.A, Be, p.C, t.row0, t.rows, t.col0, p.K, p.N, lds);
+}
+
+// MASK: bit 0 -> BM 16, bit 1 -> 32, bit 2 -> 64, bit 3 -> 128 compiled in.
+template <int MASK>
+__global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t lds_dyn[];
+  __shared__ SchedLds sched;
+  lds_u16 *const lds = (lds_u16 *)lds_dyn;
+  const int NT = cdiv(p.N, kBN);
+  const int total = build_schedule(sched, p.off, p.E, p.M_cap, NT, p.bm_fixed);
+  const int G = gridDim.x;  // a multiple of kXcds
+  const int b = blockIdx.x;
+  const int slot = (b % kXcds) * (G / kXcds) + b / kXcds;
+  for (int base = 0; base < total; base += G) {
+    const int t = base + slot;
+    if (t >= total) break;
+    const Tile tl = decode_tile(sched, t, p.E, NT, p.bm_fixed);
+    switch (tl.bm) {
+      case 16: if constexpr (MASK & 1) tile_body<Cfg16>(p, tl, lds); break;
+      case 32: if constexpr (MASK & 2) tile_body<Cfg32>(p, tl, lds); break;
+      case 64: if constexpr (MASK & 4) tile_body<Cfg64>(p, tl, lds); break;
+      default: if constexpr (MASK & 8) tile_body<Cfg128>(p, tl, lds); break;
+    }
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void tile_schedule_kernel(const int32_t *off, int E, int N,
+                                                                 int M_cap, int bm_fixed,
+                                                                 int32_t *tiles, int32_t *n_tiles,
+                                                                 int max_tiles) {
+  __shared__ SchedLds sched;
+  const int NT = cdiv(N, kBN);
+  const int total = build_schedule(sched, off, E, M_cap, NT, bm_fixed);
+  if (threadIdx.x == 0) *n_tiles = total;
+  const int lim = total < max_tiles ? total : max_tiles;
+  for (int t = threadIdx.x; t < lim; t += kThreads) {
+    const Tile tl = decode_tile(sched, t, E, NT, bm_fixed);
+    int32_t *o = tiles + 5 * (size_t)t;
+    o[0] = tl.expert;
+    o[1] = tl.row0;
+    o[2] = tl.rows;
+    o[3] = tl.col0;
+    o[4] = tl.bm;
+  }
+}
+
+template <int MASK>
+constexpr int lds_bytes() {
+  int m = 0;
+  if (MASK & 1) m = m > Cfg16::LDS_BYTES ? m : Cfg16::LDS_BYTES;
+  if (MASK & 2) m = m > Cfg32::LDS_BYTES ? m : Cfg32::LDS_BYTES;
+  if (MASK & 4) m = m > Cfg64::LDS_BYTES ? m : Cfg64::LDS_BYTES;
+  if (MASK & 8) m = m > Cfg128::LDS_BYTES ? m : Cfg128::LDS_BYTES;
+  return m;
+}
+
+// Per-device, per-variant launch limits (CU count x resident workgroups).
+struct LaunchInfo {
+  int grid = 0;
+  hipError_t err = hipSuccess;
+};
+
+constexpr int kMaxDevices = 64;
+
+template <int MASK>
+static LaunchInfo launch_info(int dev) {
+  static LaunchInfo cache[kMaxDevices];
+  static std::once_flag once[kMaxDevices];
+  std::call_once(once[dev], [dev]() {
+    LaunchInfo li;
+    int cus = 0, per_cu = 0;
+    const int lds = lds_bytes<MASK>();
+    li.err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (li.err == hipSuccess)
+      li.err = hipFuncSetAttribute((const void *)grouped_gemm_kernel<MASK>,
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (li.err == hipSuccess)
+      li.err = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &per_cu, (const void *)grouped_gemm_kernel<MASK>, kThreads, lds);
+    if (li.err == hipSuccess) {
+      if (per_cu < 1) per_cu = 1;
+      li.grid = cus * per_cu;
+      li.grid -= li.grid % kXcds;
+      if (li.grid < kXcds) li.grid = kXcds;
+    }
+    cache[dev] = li;
+  });
+  return cache[dev];
+}
+
+template <int MASK>
+static gg_status_t launch(const Params &p, long long tile_bound, hipStream_t stream) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return GG_ERR_LAUNCH;
+  const LaunchInfo li = launch_info<MASK>(dev);
+  if (li.err != hipSuccess) return GG_ERR_LAUNCH;
+  long long g = tile_bound < li.grid ? tile_bound : li.grid;
+  g = (g + kXcds - 1) / kXcds * kXcds;  // keep a multiple of the XCD count
+  hipLaunchKernelGGL(grouped_gemm_kernel<MASK>, dim3((unsigned)g), dim3(kThreads),
+                     lds_bytes<MASK>(), stream, p);
+  return hipGetLastError() == hipSuccess ? GG_OK : GG_ERR_LAUNCH;
+}
+
+static bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Shared argument checks; fills the tile-count upper bound.
+static gg_status_t check_sizes(const int32_t *off, int E, int N, int M_cap, int bm,
+                               long long *tile_bound) {
+  if (off == nullptr) return GG_ERR_INVALID_VALUE;
+  if (E < 1 || N < 1 || M_cap < 0) return GG_ERR_INVALID_VALUE;
+  if (!(bm == 0 || bm == 16 || bm == 32 || bm == 64 || bm == 128)) return GG_ERR_INVALID_VALUE;
+  if (E > kMaxExperts) return GG_ERR_UNSUPPORTED;
+  if (!aligned(off, 4)) return GG_ERR_MISALIGNED;
+  if (N % 8 != 0) return GG_ERR_MISALIGNED;
+  const long long hmin = bm ? bm : 16;
+  const long long nt = (N + kBN - 1) / kBN;
+  const long long bound = ((long long)M_cap / hmin + E) * nt;
+  // tile ids, rows + tile height and 5*tile indices must stay inside int32
+  if (bound > (1LL << 28) || (long long)M_cap + 128 > INT32_MAX) return GG_ERR_UNSUPPORTED;
+  *tile_bound = bound;
+  return GG_OK;
+}
+
+}  // namespace gg
+
+using namespace gg;
+
+extern "C" gg_status_t gg_grouped_gemm_bf16(const void *A, const void *B,
+                                            const int32_t *group_offsets, float *C, int32_t E,
+                                            int32_t K, int32_t N, int32_t M_cap, int32_t bm,
+                                            void *stream) {
+  long long bound = 0;
+  gg_status_t st = check_sizes(group_offsets, E, N, M_cap, bm, &bound);
+  if (st != GG_OK) return st;
+  if (A == nullptr || B == nullptr || C == nullptr || K < 1) return GG_ERR_INVALID_VALUE;
+  if (K % 8 != 0) return GG_ERR_MISALIGNED;
+  if (!aligned(A, 16) || !aligned(B, 16) || !aligned(C, 16)) return GG_ERR_MISALIGNED;
+  if (M_cap == 0 || bound == 0) return GG_OK;
+  Params p{static_cast<const uint16_t *>(A), static_cast<const uint16_t *>(B), group_offsets, C,
+           E, K, N, M_cap, bm};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  switch (bm) {
+    case 16: return launch<1>(p, bound, s);
+    case 32: return launch<2>(p, bound, s);
+    case 64: return launch<4>(p, bound, s);
+    case 128: return launch<8>(p, bound, s);
+    default: return launch<15>(p, bound, s);
+  }
+}
+
+extern "C" gg_status_t gg_tile_schedule(const int32_t *group_offsets, int32_t E, int32_t N,
+                                        int32_t M_cap, int32_t bm, int32_t *tiles,
+                                        int32_t *n_tiles, int32_t max_tiles, void *stream) {
+  long long bound = 0;
+  gg_status_t st = check_sizes(group_offsets, E, N, M_cap, bm, &bound);
+  if (st != GG_OK) return st;
+  if (n_tiles == nullptr || max_tiles < 0 || (max_tiles > 0 && tiles == nullptr))
+    return GG_ERR_INVALID_VALUE;
+  if (!aligned(n_tiles, 4) || (tiles && !aligned(tiles, 4))) return GG_ERR_MISALIGNED;
+  hipLaunchKernelGGL(tile_schedule_kernel, dim3(1), dim3(kThreads), 0,
+                     static_cast<hipStream_t>(stream), group_offsets, E, N, M_cap, bm, tiles,
+                     n_tiles, max_tiles);
+  return hipGetLastError() == hipSuccess ? GG_OK : GG_ERR_LAUNCH;
+}
+
+extern "C" const char *gg_status_string(gg_status_t status) {
+  switch (status) {
+    case GG_OK: return "success";
+    case GG_ERR_INVALID_VALUE: return "invalid argument (null pointer, size or tile height)";
+    case GG_ERR_MISALIGNED: return "misaligned pointer, or K or N not a multiple of 8";
+    case GG_ERR_UNSUPPORTED: return "unsupported problem (too many experts or rows)";
+    case GG_ERR_LAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}

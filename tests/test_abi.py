@@ -1,0 +1,86 @@
+"""The C-ABI library (no GPU): it loads, exports every declared symbol, and its
+host-side argument checks return the documented status without enqueuing work.
+
+None of the calls below reaches the HIP runtime: each is rejected by the host
+checks before any device call.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import moe_ragged_grouped_amd as gg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER_DIR = os.path.join(ROOT, "include")
+
+
+def _declared_symbols():
+    names = set()
+    for fn in os.listdir(HEADER_DIR):
+        if fn.endswith(".h"):
+            text = open(os.path.join(HEADER_DIR, fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names.update(re.findall(r"\b(gg_[a-z0-9_]+)\s*\(", text))
+    return names
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(gg.library_path()):
+        import moe_ragged_grouped_amd.build as b
+        b.build()
+    return gg.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = _declared_symbols()
+    assert declared == set(gg.SYMBOLS), declared
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for code in range(5):
+        assert lib.gg_status_string(code)
+    assert lib.gg_status_string(99) == b"unknown status"
+
+
+GOOD = dict(A=16, B=32, off=64, C=128, E=4, K=256, N=256, M_cap=29, bm=0)
+
+
+def _call(lib, **kw):
+    a = dict(GOOD)
+    a.update(kw)
+    # fake but aligned device addresses: every call below is rejected on the host
+    return lib.gg_grouped_gemm_bf16(a["A"], a["B"], a["off"], a["C"], a["E"], a["K"], a["N"],
+                                    a["M_cap"], a["bm"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(A=0), 1), (dict(B=0), 1), (dict(C=0), 1), (dict(off=0), 1),
+    (dict(E=0), 1), (dict(E=-3), 1), (dict(K=0), 1), (dict(N=0), 1), (dict(M_cap=-1), 1),
+    (dict(bm=8), 1), (dict(bm=256), 1), (dict(bm=48), 1),
+    (dict(A=24), 2), (dict(B=40), 2), (dict(C=8), 2), (dict(off=66), 2),
+    (dict(K=12), 2), (dict(N=100), 2),
+    (dict(E=1025), 3), (dict(M_cap=2**31 - 100), 3),
+])
+def test_host_checks(lib, kw, status):
+    assert _call(lib, **kw) == status
+
+
+def test_empty_problem_enqueues_nothing(lib):
+    # M_cap == 0: nothing to compute; returns before touching the device
+    assert _call(lib, M_cap=0) == 0
+
+
+def test_tile_schedule_host_checks(lib):
+    f = lib.gg_tile_schedule
+    assert f(64, 4, 256, 29, 0, 128, 0, 10, None) == 1     # n_tiles NULL
+    assert f(64, 4, 256, 29, 0, 0, 128, 10, None) == 1     # tiles NULL with max_tiles > 0
+    assert f(64, 4, 256, 29, 0, 128, 128, -1, None) == 1   # negative max
+    assert f(64, 4, 256, 29, 7, 128, 128, 10, None) == 1   # bad bm
+    assert f(64, 4, 250, 29, 0, 128, 128, 10, None) == 2   # N not multiple of 8
+    assert f(0, 4, 256, 29, 0, 128, 128, 10, None) == 1    # offsets NULL

@@ -1,0 +1,233 @@
+"""HIP path vs the CPU oracle, element by element (needs an MI355X).
+
+Small problems are compared whole: they span several 128-column tiles, several
+64-deep K slices with a partial last slice, experts smaller than one tile,
+experts spanning many tiles and empty experts. The full-size workloads are
+compared on sampled entries the oracle computes one dot product at a time,
+plus properties that hold at any size (every routed row written and finite,
+rows past the last group untouched).
+"""
+
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+from tests import parity
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+BMS = [0, 16, 32, 64, 128]
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def gg():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import moe_ragged_grouped_amd as m
+    m.load_library()
+    return m
+
+
+def _dev(w, guard_rows=0):
+    dev = torch.device("cuda:0")
+    A = torch.from_numpy(w.A.view(np.int16)).to(dev).view(torch.bfloat16)
+    B = torch.from_numpy(w.B.view(np.int16)).to(dev).view(torch.bfloat16)
+    off = torch.from_numpy(w.offsets).to(dev)
+    return A, B, off
+
+
+def _run(gg, w, bm, C=None):
+    A, B, off = _dev(w)
+    if C is None:
+        C = torch.full((w.M_cap, w.N), float("nan"), dtype=torch.float32, device="cuda:0")
+    gg.grouped_gemm(A, B, off, out=C, bm=bm)
+    torch.cuda.synchronize()
+    return C.cpu().numpy()
+
+
+def _full_compare(gg, w, bm, what):
+    _say("case %s E=%d K=%d N=%d M_tot=%d M_cap=%d bm=%d" % (what, w.E, w.K, w.N, w.M_tot, w.M_cap, bm))
+    got = _run(gg, w, bm)
+    ref, s, _ = oracle.grouped_gemm(w.A, w.B, w.offsets)
+    m = w.M_tot
+    parity.check(got[:m], ref[:m], s[:m], what)
+    assert np.isnan(got[m:]).all(), "%s: rows past the last group were written" % what
+    return got, ref
+
+
+@pytest.mark.parametrize("bm", BMS)
+def test_tiny(gg, bm):
+    _full_compare(gg, wl.make_workload("tiny"), bm, "tiny")
+
+
+@pytest.mark.parametrize("bm", BMS)
+def test_ragged_multi_tile(gg, bm):
+    w = wl.make_workload(E=6, K=328, N=392, sizes=[0, 1, 17, 130, 0, 300], seed=21, M_cap=470)
+    _full_compare(gg, w, bm, "ragged")
+
+
+@pytest.mark.parametrize("bm", BMS)
+def test_integer_inputs_bit_exact(gg, bm):
+    # integer bf16 in [-3,3], K=512: every partial sum is an integer below 2^24,
+    # so any fp32 accumulation order gives the exact value
+    w = wl.make_workload(E=5, K=512, N=264, sizes=[5, 0, 40, 129, 16], seed=22, values="int")
+    _say("case int-exact bm=%d" % bm)
+    got = _run(gg, w, bm)
+    ref, _, _ = oracle.grouped_gemm(w.A, w.B, w.offsets, want_s=False)
+    assert (got == ref).all()
+
+
+@pytest.mark.parametrize("bm", [0, 16, 128])
+def test_identity_weights(gg, bm):
+    w = wl.make_workload("tiny")
+    eye = wl.f32_to_bf16_bits(np.eye(256, dtype=np.float32))
+    w.B = np.broadcast_to(eye, (4, 256, 256)).copy()
+    _say("case identity bm=%d" % bm)
+    got = _run(gg, w, bm)
+    assert (got == wl.bf16_bits_to_f32(w.A)).all()
+
+
+@pytest.mark.parametrize("sizes", [[0, 0, 5, 3], [4, 2, 0, 0], [3, 0, 0, 4], [0, 0, 0, 0], [0], [0, 200, 0]])
+@pytest.mark.parametrize("bm", [0, 32])
+def test_empty_groups(gg, sizes, bm):
+    w = wl.make_workload(E=len(sizes), K=64, N=136, sizes=sizes, seed=23, M_cap=sum(sizes) + 5)
+    _full_compare(gg, w, bm, "empty%s" % sizes)
+
+
+@pytest.mark.parametrize("bm", [0, 64])
+def test_group_split_invariance(gg, bm):
+    w = wl.make_workload(E=2, K=200, N=256, sizes=[150, 40], seed=24)
+    _say("case split bm=%d" % bm)
+    got = _run(gg, w, bm)
+    w2 = wl.make_workload(E=2, K=200, N=256, sizes=[150, 40], seed=24)
+    w2.offsets = np.array([0, 70, 150, 190], dtype=np.int32)
+    w2.B = np.ascontiguousarray(np.stack([w.B[0], w.B[0], w.B[1]]))
+    w2.E = 3
+    got2 = _run(gg, w2, bm)
+    # each output element sums the same products in the same k order in any tile
+    assert (got == got2).all()
+
+
+def test_repeat_is_deterministic(gg):
+    w = wl.make_workload(E=6, K=328, N=392, sizes=[0, 1, 17, 130, 0, 300], seed=25)
+    _say("case repeat")
+    a = _run(gg, w, 0)
+    b = _run(gg, w, 0)
+    assert (a == b).all()
+
+
+@pytest.mark.parametrize("sizes", [[3, 0, 17, 9], [0, 0, 1], [129, 0, 1000, 31, 16, 0, 2]])
+@pytest.mark.parametrize("bm", BMS)
+@pytest.mark.parametrize("N", [256, 392])
+def test_tile_schedule_matches_oracle(gg, sizes, bm, N):
+    off = wl.offsets_from_sizes(sizes)
+    M_cap = int(off[-1]) + 7
+    _say("case schedule %s bm=%d N=%d" % (sizes, bm, N))
+    tiles, n = gg.tile_schedule(torch.from_numpy(off).cuda(), N, M_cap, bm)
+    bms = oracle.adaptive_bm(sizes) if bm == 0 else bm
+    ref = oracle.tile_list(off, N, bms, gg.TILE_N)
+    assert n == len(ref)
+    got = [tuple(int(v) for v in r) for r in tiles.cpu().numpy()]
+    hs = bms if bm == 0 else [bm] * len(sizes)
+    assert got == [t + (hs[t[0]],) for t in ref]
+
+
+def test_tile_schedule_page_counts(gg):
+    # worklog section 3: 2,688 / 3,444 tiles at 128x128, balanced / skewed 16k
+    for sizes, bm, count in (([256] * 64, 128, 2688), (list(wl.page_skew_sizes(16384, 64, 1.2)), 128, 3444),
+                             ([256] * 64, 32, 10752)):
+        off = torch.from_numpy(wl.offsets_from_sizes(sizes)).cuda()
+        _, n = gg.tile_schedule(off, 2688, 16384, bm, max_tiles=0)
+        assert n == count
+
+
+def test_malformed_offsets_stay_in_bounds(gg):
+    w = wl.make_workload(E=4, K=64, N=128, sizes=[10, 10, 10, 10], seed=26)
+    dev = torch.device("cuda:0")
+    A, B, _ = _dev(w)
+    ref, s, _ = oracle.grouped_gemm(w.A, w.B, w.offsets)
+    guard = 8
+    for bad in ([-5, 10, 5, 30, 40], [0, 10, 20, 30, 99], [0, 50, 20, 30, 40]):
+        _say("case malformed %s" % bad)
+        Cbig = torch.full((w.M_cap + guard, w.N), float("nan"), dtype=torch.float32, device=dev)
+        C = Cbig[: w.M_cap]
+        off = torch.tensor(bad, dtype=torch.int32, device=dev)
+        # the library sees M_cap = 40; nothing may land in the guard rows
+        import moe_ragged_grouped_amd as m
+        m.grouped_gemm(A, B, off, out=C, bm=0)
+        torch.cuda.synchronize()
+        out = Cbig.cpu().numpy()
+        assert np.isnan(out[w.M_cap:]).all()
+    # offsets [0,10,20,30,99] clamp to [0,10,20,30,40]: the well-formed product
+    Cw = torch.full((w.M_cap, w.N), float("nan"), dtype=torch.float32, device=dev)
+    m.grouped_gemm(A, B, torch.tensor([0, 10, 20, 30, 99], dtype=torch.int32, device=dev), out=Cw)
+    torch.cuda.synchronize()
+    parity.check(Cw.cpu().numpy(), ref, s, "clamped")
+
+
+# ---- full-size workloads, sampled ------------------------------------------------
+
+FULL = ["decode", "uniform16k", "skew16k", "skew2k_wide"]
+_cache = {}
+
+
+def _full(name):
+    if name not in _cache:
+        _cache.clear()
+        _say("drawing workload %s" % name)
+        _cache[name] = wl.make_workload(name, M_cap=None)
+    return _cache[name]
+
+
+def _samples(w, rng, n_random=3000):
+    rows, cols = [], []
+    off = w.offsets
+    for e in range(w.E):
+        r0, r1 = int(off[e]), int(off[e + 1])
+        if r1 > r0:
+            for r in {r0, r1 - 1, (r0 + r1) // 2}:
+                for c in (0, 1, 127, 128, w.N - 1, int(rng.integers(0, w.N))):
+                    rows.append(r)
+                    cols.append(c)
+    rows += list(rng.integers(0, w.M_tot, size=n_random))
+    cols += list(rng.integers(0, w.N, size=n_random))
+    return np.array(rows, dtype=np.int64), np.array(cols, dtype=np.int64)
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled(gg, name):
+    w = _full(name)
+    guard = 16
+    dev = torch.device("cuda:0")
+    A, B, off = _dev(w)
+    Cbig = torch.full((w.M_cap + guard, w.N), float("nan"), dtype=torch.float32, device=dev)
+    _say("case full %s E=%d K=%d N=%d M_tot=%d bm=0" % (name, w.E, w.K, w.N, w.M_tot))
+    gg.grouped_gemm(A, B, off, out=Cbig[: w.M_cap], bm=0)
+    torch.cuda.synchronize()
+    out = Cbig.cpu().numpy()
+    assert np.isfinite(out[: w.M_tot]).all(), "unwritten or non-finite routed rows"
+    assert np.isnan(out[w.M_cap:]).all(), "write past M_cap"
+    rng = np.random.default_rng(7)
+    rows, cols = _samples(w, rng)
+    c, s = oracle.grouped_gemm_entries(w.A, w.B, w.offsets, rows, cols)
+    got = out[rows, cols]
+    d = np.abs(got - c)
+    assert (d <= parity.ELEM * s).all(), "worst ratio %.3e" % float(np.max(d / s))
+    rel = np.linalg.norm(got - c) / np.linalg.norm(c)
+    assert rel <= parity.REL_FRO
+    # one whole 128x128 output block of the largest expert, entry by entry
+    e = int(np.argmax(w.sizes))
+    r0 = int(w.offsets[e])
+    nr = min(128, int(w.sizes[e]))
+    rr, cc = np.meshgrid(np.arange(r0, r0 + nr), np.arange(128, 256), indexing="ij")
+    c2, s2 = oracle.grouped_gemm_entries(w.A, w.B, w.offsets, rr.ravel(), cc.ravel())
+    parity.check(out[rr.ravel(), cc.ravel()], c2, s2, name + " block")

@@ -20,15 +20,19 @@ What is drawn, and why it looks like the pages' workloads:
   the top 16 bits of an IEEE binary32 word; the rounding below is the
   textbook round-half-even on the 16 discarded bits (inputs are finite).
 
-Draw order inside one workload: routing, then A, then B (B one expert at a
-time, so the 805M-element weight tensors of the 6144x4096 shapes are drawn
-in bounded chunks).
+Streams: the group sizes come from numpy's PCG64 generator seeded with the
+workload seed; A from ``default_rng([seed, 1])``; expert e's weight slice
+from ``default_rng([seed, 2, e])``. Giving every expert its own stream keeps
+the 805M-element weight tensors of the 6144x4096 shapes deterministic while
+they are drawn in parallel threads, one bounded slice at a time.
 """
 
 from __future__ import annotations
 
 import dataclasses
 import math
+import os
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
@@ -45,13 +49,22 @@ __all__ = [
 ]
 
 
-def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
-    """Round float32 -> bfloat16 bit patterns (uint16), nearest, ties to even."""
-    x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    lsb = (u >> np.uint64(16)) & np.uint64(1)
-    r = (u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)
-    return r.astype(np.uint16)
+def f32_to_bf16_bits(x: np.ndarray, out: np.ndarray = None) -> np.ndarray:
+    """Round finite float32 -> bfloat16 bit patterns (uint16), nearest, ties to even.
+
+    Works in uint32: for every finite pattern u, u + 0x7FFF + 1 < 2^32, so the
+    biased sum cannot wrap.
+    """
+    u = np.array(x, dtype=np.float32, copy=True, order="C").view(np.uint32)
+    lsb = u >> np.uint32(16)
+    lsb &= np.uint32(1)
+    u += np.uint32(0x7FFF)
+    u += lsb
+    u >>= np.uint32(16)
+    if out is None:
+        return u.astype(np.uint16)
+    out[...] = u
+    return out
 
 
 def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
@@ -184,15 +197,23 @@ def make_workload(name: str = None, *, E=None, K=None, N=None, sizes=None, scale
         M_cap = m_tot
     assert M_cap >= m_tot
     A = np.zeros((M_cap, K), dtype=np.uint16)
-    B = np.zeros((E, K, N), dtype=np.uint16)
-    if values == "int":
-        A[:m_tot] = f32_to_bf16_bits(rng.integers(-3, 4, size=(m_tot, K)).astype(np.float32))
-        for e in range(E):
-            B[e] = f32_to_bf16_bits(rng.integers(-3, 4, size=(K, N)).astype(np.float32))
-    else:
-        sc = _scale(scale, K)
-        A[:m_tot] = f32_to_bf16_bits(rng.standard_normal((m_tot, K), dtype=np.float32) * sc)
-        for e in range(E):
-            B[e] = f32_to_bf16_bits(rng.standard_normal((K, N), dtype=np.float32) * sc)
+    B = np.empty((E, K, N), dtype=np.uint16)
+    sc = _scale(scale, K)
+
+    def draw(r, shape):
+        if values == "int":
+            return r.integers(-3, 4, size=shape).astype(np.float32)
+        x = r.standard_normal(shape, dtype=np.float32)
+        x *= sc
+        return x
+
+    f32_to_bf16_bits(draw(np.random.default_rng([seed, 1]), (m_tot, K)), out=A[:m_tot])
+
+    def draw_expert(e):
+        f32_to_bf16_bits(draw(np.random.default_rng([seed, 2, e]), (K, N)), out=B[e])
+
+    workers = max(1, min(16, os.cpu_count() or 1, E))
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        list(ex.map(draw_expert, range(E)))
     return Workload(name=name or "custom", E=E, K=K, N=N, sizes=sizes, offsets=off,
                     M_cap=M_cap, A=A, B=B, seed=seed)

@@ -65,8 +65,8 @@ typedef enum {
  *       product (not accumulated into); rows [M_tot, M_cap) are not touched.
  *   E in [1, GG_MAX_EXPERTS]; K >= 8 and N >= 8, both multiples of 8;
  *   M_cap >= 0 (0: nothing is enqueued).
- *   bm  tile height: 16, 32, 64 or 128 for every expert, or 0 to let the
- *       device choose per expert from its row count (the trade between
+ *   bm  tile height: 16, 32, 64, 128 or 256 for every expert, or 0 to let
+ *       the device choose per expert from its row count (the trade between
  *       padding in the last tile and per-tile work that the worklog
  *       describes in sections 2.1, 6 and 7).
  *   A, B and C must be 16-byte aligned; group_offsets 4-byte aligned.
@@ -87,10 +87,13 @@ gg_status_t gg_grouped_gemm_bf16(const void *A, const void *B, const int32_t *gr
  * The device builds it from group_offsets with exactly the code the product
  * kernel runs; tile t of the list is written as 5 int32
  *     tiles[5t .. 5t+4] = { expert, row0, rows, col0, bm }
- * in tile-id order (expert, then M tile, then N tile innermost). col0 steps
- * by the tile width of the chosen tile height (128 columns for every height
- * in this version). At most max_tiles descriptors are written; *n_tiles (a
- * device int32) receives the full count even when it exceeds max_tiles.
+ * in the order the product kernel walks tile ids. The set of descriptors is
+ * the worklog's; the order is expert by expert, and inside an expert the M
+ * tiles are taken in groups of up to 8 with the N tile outer and the M tile
+ * inner in each group (so consecutive tiles share a column slice of the
+ * expert's weights). Tiles are 128 columns wide for every height. At most
+ * max_tiles descriptors are written; *n_tiles (a device int32) receives the
+ * full count even when it exceeds max_tiles.
  * Arguments E, N, M_cap, bm and the offsets rules are those of
  * gg_grouped_gemm_bf16; tiles may be NULL when max_tiles == 0.
  */

@@ -15,13 +15,14 @@ import ctypes
 import os
 
 __all__ = ["grouped_gemm", "tile_schedule", "library_path", "load_library", "GroupedGemmError",
-           "BM_CHOICES", "TILE_N", "MAX_EXPERTS", "SYMBOLS"]
+           "BM_CHOICES", "TILE_N", "TILE_WIDTH", "MAX_EXPERTS", "SYMBOLS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libmoe_ragged_grouped_amd.so")
 
-BM_CHOICES = (16, 32, 64, 128)
-TILE_N = 128
+BM_CHOICES = (16, 32, 64, 128, 256)
+TILE_N = 128                      # narrowest tile width
+TILE_WIDTH = {16: 128, 32: 128, 64: 128, 128: 128, 256: 128}  # per tile height
 MAX_EXPERTS = 1024
 SYMBOLS = ("gg_grouped_gemm_bf16", "gg_tile_schedule", "gg_status_string")
 
@@ -73,7 +74,7 @@ def grouped_gemm(A, B, offsets, out=None, bm: int = 0, stream=None):
 
     A: bf16 [M_cap, K]; B: bf16 [E, K, N]; offsets: int32 [E+1] (device);
     out: optional fp32 [M_cap, N]; bm: 0 (per-expert choice on the device)
-    or 16/32/64/128. Rows of ``out`` at or past offsets[E] are left as they
+    or 16/32/64/128/256. Rows of ``out`` at or past offsets[E] are left as they
     were. Enqueued on ``stream`` (default: torch's current stream).
     """
     import torch

@@ -24,10 +24,18 @@ constexpr int kWave = 64;
 
 __device__ __forceinline__ int cdiv(int a, int b) { return (a + b - 1) / b; }
 
+// Global-memory typed pointers: keep loads and stores global_* instructions
+// even where the compiler cannot see where a pointer came from (a generic
+// pointer would become flat_* accesses, which also count against the LDS
+// wait counter).
+typedef __attribute__((address_space(1))) const u32x4 gbl_cu32x4;
+typedef __attribute__((address_space(1))) f32x4 gbl_f32x4;
+
 // One 16-byte global load (global_load_dwordx4).
-__device__ __forceinline__ u32x4 ld_g16(const void *p) {
-  return *reinterpret_cast<const u32x4 *>(p);
-}
+__device__ __forceinline__ u32x4 ld_g16(const void *p) { return *(gbl_cu32x4 *)p; }
+
+// One 16-byte global store (global_store_dwordx4).
+__device__ __forceinline__ void st_g16(float *p, f32x4 v) { *(gbl_f32x4 *)p = v; }
 
 // Transposing LDS read of a 4 (rows) x 16 (16-bit columns) block per 16-lane
 // group (ds_read_b64_tr_b16). Lane 16g + s supplies the address of 4

@@ -7,28 +7,36 @@
 // register-direct epilogue of section 4.1).
 //
 // MI355X mapping:
+//  * Two workgroups of four waves per CU (at most 256 registers per wave, at
+//    most 80 KiB of LDS per workgroup): for the weight-streaming shapes the
+//    bytes in flight per CU, not the tile shape, set the achieved HBM
+//    bandwidth, and a second resident workgroup doubles them.
+//  * K runs in slices of BK: every thread moves 16-byte chunks global ->
+//    registers (global_load_dwordx4) for slice k+1 while the matrix cores work
+//    on slice k out of LDS, then writes them to the other of two LDS stages
+//    (ds_write_b128); one barrier per slice.
 //  * v_mfma_f32_16x16x32_bf16 computes C^T blocks: the first operand is a
 //    16 (n) x 32 (k) slice of B^T, the second a 32 (k) x 16 (m) slice of A^T.
-//    Both operands then want 8 consecutive k per lane. A rows are already
-//    K-contiguous (one 16-byte LDS read per lane); B is [K][N] N-contiguous,
-//    so its fragments come from ds_read_b64_tr_b16, which transposes a
-//    4 x 16 row-major block per 16-lane group on the way out of LDS.
+//    Both operands want 8 consecutive k per lane. A rows are K-contiguous in
+//    LDS (one ds_read_b128 per lane); B is [K][N] N-contiguous, and its
+//    fragments come from ds_read_b64_tr_b16, which transposes a 4 x 16
+//    row-major block per 16-lane group on the way out of LDS. Rows of both
+//    stages are padded by 16 bytes. The transposing read moves about 97 bytes
+//    per clock per CU against 172 for ds_read_b128, so tall wave tiles (fewer
+//    B fragments per flop) are preferred.
 //  * The accumulator layout of C^T gives every lane 4 consecutive columns of
 //    one row of C, so the epilogue is one 16-byte store per lane per block,
 //    straight from registers with a per-lane row guard.
-//  * Global -> LDS staging: every thread moves 16-byte chunks
-//    (global_load_dwordx4 / ds_write_b128); the next K slice is fetched into
-//    registers while the matrix cores work on the current LDS stage (two LDS
-//    stages, one barrier per K slice).
 #pragma once
 
 #include "gg_common.h"
+#include "gg_schedule.h"
 
 namespace gg {
 
-template <int BM_, int BN_, int BK_, int WM_, int WN_>
+template <int BM_, int BK_, int WM_, int WN_>
 struct TileCfg {
-  static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_;
+  static constexpr int BM = BM_, BN = width_of(BM_), BK = BK_, WM = WM_, WN = WN_;
   static_assert(WM * WN == kThreads / kWave, "four waves per workgroup");
   static constexpr int WTM = BM / WM;  // rows of C per wave
   static constexpr int WTN = BN / WN;  // columns of C per wave
@@ -46,11 +54,19 @@ struct TileCfg {
   static constexpr int LDS_BYTES = 2 * (A_STAGE + B_STAGE) * 2;
 };
 
-// Tile configurations per tile height (the tile width is 128 for all).
-using Cfg16 = TileCfg<16, 128, 64, 1, 4>;
-using Cfg32 = TileCfg<32, 128, 64, 1, 4>;
-using Cfg64 = TileCfg<64, 128, 64, 1, 4>;
-using Cfg128 = TileCfg<128, 128, 64, 2, 2>;
+// Tile configurations per tile height (all 128 columns wide).
+using Cfg16 = TileCfg<16, 64, 1, 4>;    // wave tile 16 x 32
+using Cfg32 = TileCfg<32, 64, 1, 4>;    // wave tile 32 x 32
+using Cfg64 = TileCfg<64, 64, 1, 4>;    // wave tile 64 x 32
+using Cfg128 = TileCfg<128, 64, 2, 2>;  // wave tile 64 x 64
+using Cfg256 = TileCfg<256, 32, 2, 2>;  // wave tile 128 x 64 (32-deep slices fit 2 stages)
+
+struct TileArgs {
+  const uint16_t *A;   // A rows of this tile: row r at A + r * K
+  const uint16_t *B;   // B[e] + col0: element (k, n) at B + k * N + n
+  float *C;            // C + row0 * N + col0
+  int rows, K, N, ncols;  // ncols = valid columns in this tile (<= BN)
+};
 
 template <class C>
 struct Staging {
@@ -58,11 +74,10 @@ struct Staging {
   u32x4 b[C::B_PER_T];
 };
 
-// Global -> registers for K slice starting at k0. Out-of-range chunks are zero.
+// Global -> registers for the K slice starting at k0. Out-of-range chunks
+// (rows past the tile's valid rows, K past the end, columns past N) are zero.
 template <class C>
-__device__ __forceinline__ void load_slice(Staging<C> &st, const uint16_t *__restrict__ A,
-                                           const uint16_t *__restrict__ Be, int row0, int rows,
-                                           int col0, int k0, int K, int N) {
+__device__ __forceinline__ void load_slice(Staging<C> &st, const TileArgs &t, int k0) {
   const int tid = threadIdx.x;
 #pragma unroll
   for (int i = 0; i < C::A_PER_T; ++i) {
@@ -70,21 +85,21 @@ __device__ __forceinline__ void load_slice(Staging<C> &st, const uint16_t *__res
     const int r = c / (C::BK / 8), kc = c % (C::BK / 8);
     const int k = k0 + 8 * kc;
     u32x4 v = {0u, 0u, 0u, 0u};
-    if (c < C::A_CHUNKS && r < rows && k < K) v = ld_g16(A + (size_t)(row0 + r) * K + k);
+    if (c < C::A_CHUNKS && r < t.rows && k < t.K) v = ld_g16(t.A + (size_t)r * t.K + k);
     st.a[i] = v;
   }
 #pragma unroll
   for (int i = 0; i < C::B_PER_T; ++i) {
     const int c = tid + i * kThreads;
     const int kr = c / (C::BN / 8), nc = c % (C::BN / 8);
-    const int k = k0 + kr, n = col0 + 8 * nc;
+    const int k = k0 + kr, n = 8 * nc;
     u32x4 v = {0u, 0u, 0u, 0u};
-    if (c < C::B_CHUNKS && k < K && n < N) v = ld_g16(Be + (size_t)k * N + n);
+    if (c < C::B_CHUNKS && k < t.K && n < t.ncols) v = ld_g16(t.B + (size_t)k * t.N + n);
     st.b[i] = v;
   }
 }
 
-// Registers -> LDS stage.
+// Registers -> one LDS stage.
 template <class C>
 __device__ __forceinline__ void store_slice(const Staging<C> &st, lds_u16 *As, lds_u16 *Bs) {
   const int tid = threadIdx.x;
@@ -102,7 +117,9 @@ __device__ __forceinline__ void store_slice(const Staging<C> &st, lds_u16 *As, l
   }
 }
 
-// Matrix-core work on one LDS stage.
+// Matrix-core work on one LDS stage (BK/32 K steps of 32). The B fragments
+// of a step are read first and kept; the A fragments are streamed one 16-row
+// block at a time, which keeps a tall wave tile's register footprint small.
 template <class C>
 __device__ __forceinline__ void mma_stage(f32x4 (&acc)[C::NI][C::MI], const lds_u16 *As,
                                           const lds_u16 *Bs, int wm0, int wn0) {
@@ -110,12 +127,6 @@ __device__ __forceinline__ void mma_stage(f32x4 (&acc)[C::NI][C::MI], const lds_
   const int g = lane / 16, s = lane % 16;
 #pragma unroll
   for (int ks = 0; ks < C::BK / 32; ++ks) {
-    bf16x8 y[C::MI];
-#pragma unroll
-    for (int mi = 0; mi < C::MI; ++mi) {
-      const lds_u16 *p = As + (wm0 + mi * 16 + s) * C::A_LD + ks * 32 + 8 * g;
-      y[mi] = __builtin_bit_cast(bf16x8, *(const lds_u32x4 *)p);
-    }
     bf16x8 x[C::NI];
 #pragma unroll
     for (int ni = 0; ni < C::NI; ++ni) {
@@ -126,22 +137,22 @@ __device__ __forceinline__ void mma_stage(f32x4 (&acc)[C::NI][C::MI], const lds_
       x[ni] = __builtin_bit_cast(bf16x8, v);
     }
 #pragma unroll
-    for (int ni = 0; ni < C::NI; ++ni)
+    for (int mi = 0; mi < C::MI; ++mi) {
+      const lds_u16 *p = As + (wm0 + mi * 16 + s) * C::A_LD + ks * 32 + 8 * g;
+      const bf16x8 y = __builtin_bit_cast(bf16x8, *(const lds_u32x4 *)p);
 #pragma unroll
-      for (int mi = 0; mi < C::MI; ++mi)
-        acc[ni][mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x[ni], y[mi], acc[ni][mi], 0, 0, 0);
+      for (int ni = 0; ni < C::NI; ++ni)
+        acc[ni][mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x[ni], y, acc[ni][mi], 0, 0, 0);
+    }
   }
 }
 
-// Full K loop and epilogue for one tile. lds must hold C::LDS_BYTES.
-// Ends with a workgroup barrier, so the caller may reuse the LDS at once.
+// Full K loop and epilogue for one tile. lds must hold C::LDS_BYTES. Ends with
+// a workgroup barrier, so the next tile may refill the stages at once.
 template <class C>
-__device__ __forceinline__ void run_tile(const uint16_t *__restrict__ A,
-                                         const uint16_t *__restrict__ Be, float *__restrict__ Cout,
-                                         int row0, int rows, int col0, int K, int N, lds_u16 *lds) {
-  // stage s: A at lds + s * A_STAGE, B at lds + 2 * A_STAGE + s * B_STAGE
-  lds_u16 *const As0 = lds;
-  lds_u16 *const Bs0 = lds + 2 * C::A_STAGE;
+__device__ __forceinline__ void run_tile(const TileArgs &t, lds_u16 *lds) {
+  lds_u16 *const As0 = lds;                       // stage s: As0 + s * A_STAGE
+  lds_u16 *const Bs0 = lds + 2 * C::A_STAGE;      // stage s: Bs0 + s * B_STAGE
   const int wave = threadIdx.x / kWave;
   const int wm0 = (wave / C::WN) * C::WTM;
   const int wn0 = (wave % C::WN) * C::WTN;
@@ -152,15 +163,15 @@ __device__ __forceinline__ void run_tile(const uint16_t *__restrict__ A,
 #pragma unroll
     for (int mi = 0; mi < C::MI; ++mi) acc[ni][mi] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int KT = cdiv(K, C::BK);
+  const int KT = cdiv(t.K, C::BK);
   Staging<C> st;
-  load_slice<C>(st, A, Be, row0, rows, col0, 0, K, N);
+  load_slice<C>(st, t, 0);
   store_slice<C>(st, As0, Bs0);
   __syncthreads();
   for (int kt = 0; kt < KT; ++kt) {
     const bool more = kt + 1 < KT;
     const int cur = kt & 1, nxt = cur ^ 1;
-    if (more) load_slice<C>(st, A, Be, row0, rows, col0, (kt + 1) * C::BK, K, N);
+    if (more) load_slice<C>(st, t, (kt + 1) * C::BK);
     mma_stage<C>(acc, As0 + cur * C::A_STAGE, Bs0 + cur * C::B_STAGE, wm0, wn0);
     if (more) store_slice<C>(st, As0 + nxt * C::A_STAGE, Bs0 + nxt * C::B_STAGE);
     __syncthreads();
@@ -172,12 +183,12 @@ __device__ __forceinline__ void run_tile(const uint16_t *__restrict__ A,
 #pragma unroll
   for (int mi = 0; mi < C::MI; ++mi) {
     const int m = wm0 + mi * 16 + s;
-    if (m < rows) {
-      float *crow = Cout + (size_t)(row0 + m) * N;
+    if (m < t.rows) {
+      float *crow = t.C + (size_t)m * t.N;
 #pragma unroll
       for (int ni = 0; ni < C::NI; ++ni) {
-        const int n = col0 + wn0 + ni * 16 + 4 * g;
-        if (n < N) *reinterpret_cast<f32x4 *>(crow + n) = acc[ni][mi];
+        const int n = wn0 + ni * 16 + 4 * g;
+        if (n < t.ncols) st_g16(crow + n, acc[ni][mi]);
       }
     }
   }

@@ -4,38 +4,52 @@
 // (The Grouped Problem and the flat tile list): every output tile of every
 // expert becomes one descriptor {expert, first row, valid rows, first column};
 // tiles stop at expert boundaries, an expert with no rows has no tiles, and
-// the descriptors are ordered expert-major with the N tile innermost. The
-// worklog enumerates the list on the host; here every workgroup rebuilds the
-// per-expert prefix of tile counts in LDS from the device-resident offsets
-// (the InferenceX glossary entry "Grouped GEMM", "Engineering details", notes
-// the same move of group-metadata generation into the kernel), so the host
-// never needs the group sizes and no device-to-host copy sits in front of the
-// launch. A tile id is decoded by binary search over that prefix.
+// the experts follow each other in order. The worklog enumerates the list on
+// the host; here every workgroup rebuilds the per-expert prefix of tile counts
+// in LDS from the device-resident offsets (the InferenceX glossary entry
+// "Grouped GEMM", "Engineering details", describes the same move of group
+// metadata generation into the kernel), so the host never needs the group
+// sizes and no device-to-host copy sits in front of the launch. A tile id is
+// decoded by binary search over that prefix.
+//
+// Order inside one expert. The worklog runs N tiles innermost. Here the M
+// tiles of an expert are taken in groups of up to kGroupM; inside a group the
+// N tile is the outer index and the M tile the inner one. Consecutive tile ids
+// then share a column slice of the expert's weights (the bulk of the bytes
+// when N*K dwarfs m_e*K), and a group's A rows stay hot across its N tiles.
+// Experts with at most kGroupM M tiles are simply N-major. The set of tiles is
+// the worklog's; only the order differs.
 #pragma once
 
 #include "gg_common.h"
 
 namespace gg {
 
-constexpr int kMaxExperts = 1024;  // per-expert tables live in LDS
+constexpr int kMaxExperts = 1024;  // the tile prefix lives in LDS
+constexpr int kGroupM = 8;         // M tiles per group in the within-expert order
 
-// Tile heights this library runs, smallest first. Tile width is 128 for all.
-constexpr int kBN = 128;
+// Tile heights this library runs, smallest first; every tile is 128 columns
+// wide.
+constexpr int kNumHeights = 5;
+__host__ __device__ constexpr int height_of(int cls) { return 16 << cls; }
+__host__ __device__ constexpr int width_of(int) { return 128; }
 
 // Per-expert tile height when the caller leaves the choice to the device.
-// Minimises ceil(m/BM) * (BM + 64) over BM in {16, 32, 64, 128}: the first
-// factor counts tiles, the second prices one tile as its rows plus a fixed
-// 64-row-equivalent share for the work every tile repeats regardless of its
-// height (streaming the expert's weight slice, barriers, epilogue set-up).
-// Ties go to the larger height; an expert with no rows gets 16 (no tiles).
+// Minimises ceil(m/BM) * (BM + 64) over BM in {16, 32, 64, 128, 256}: the
+// first factor counts tiles, the second prices one tile as its rows plus a
+// fixed 64-row-equivalent share for the work every tile repeats regardless of
+// its height (streaming the expert's weight slice, barriers, epilogue
+// set-up). Ties go to the larger height; an expert with no rows gets 16 (no
+// tiles).
 __device__ __forceinline__ int adaptive_bm(int m) {
   if (m <= 0) return 16;
   int best = 16;
   long long best_cost = (long long)cdiv(m, 16) * (16 + 64);
 #pragma unroll
-  for (int b = 32; b <= 128; b *= 2) {
-    const long long c = (long long)cdiv(m, b) * (b + 64);
-    if (c <= best_cost) { best = b; best_cost = c; }
+  for (int c = 1; c < kNumHeights; ++c) {
+    const int b = height_of(c);
+    const long long cost = (long long)cdiv(m, b) * (b + 64);
+    if (cost <= best_cost) { best = b; best_cost = cost; }
   }
   return best;
 }
@@ -45,42 +59,44 @@ struct Tile {
   int row0;   // first row in A and C
   int rows;   // valid rows, 1..bm
   int col0;   // first column in C
-  int bm;     // tile height
+  int bm;     // tile height (the width is width_of(bm))
 };
 
-// LDS tables: clamped offsets and the exclusive prefix of tile counts.
+// LDS table: exclusive prefix of tile counts per expert (start[E] = total).
 struct SchedLds {
-  int off[kMaxExperts + 1];
   int start[kMaxExperts + 1];
   int wave_sum[kThreads / kWave];
 };
 
+// Clamped group boundaries: every offset is pulled into [0, M_cap].
+__device__ __forceinline__ int clamp_off(const int32_t *off_g, int e, int M_cap) {
+  const int v = off_g[e];
+  return v < 0 ? 0 : (v > M_cap ? M_cap : v);
+}
+
 // All threads of the workgroup must call this (it contains barriers).
 // bm_fixed = 0 selects adaptive_bm per expert. Returns the total tile count.
 __device__ inline int build_schedule(SchedLds &s, const int32_t *__restrict__ off_g, int E,
-                                     int M_cap, int NT, int bm_fixed) {
+                                     int M_cap, int N, int bm_fixed) {
   const int tid = threadIdx.x;
-  for (int e = tid; e <= E; e += kThreads) {
-    int v = off_g[e];
-    v = v < 0 ? 0 : (v > M_cap ? M_cap : v);
-    s.off[e] = v;
-  }
-  __syncthreads();
   // each thread owns a run of consecutive experts (E <= 1024 -> at most 4)
   constexpr int kRun = kMaxExperts / kThreads;
   const int e0 = tid * kRun;
   int cnt[kRun];
   int local = 0;
+  int lo = e0 < E ? clamp_off(off_g, e0, M_cap) : 0;
 #pragma unroll
   for (int j = 0; j < kRun; ++j) {
     const int e = e0 + j;
     int c = 0;
     if (e < E) {
-      const int m = s.off[e + 1] - s.off[e];
+      const int hi = clamp_off(off_g, e + 1, M_cap);
+      const int m = hi - lo;
       if (m > 0) {
         const int b = bm_fixed ? bm_fixed : adaptive_bm(m);
-        c = cdiv(m, b) * NT;
+        c = cdiv(m, b) * cdiv(N, width_of(b));
       }
+      lo = hi;
     }
     cnt[j] = c;
     local += c;
@@ -115,23 +131,33 @@ __device__ inline int build_schedule(SchedLds &s, const int32_t *__restrict__ of
 }
 
 // Decode tile id t (0 <= t < total) into its descriptor.
-__device__ __forceinline__ Tile decode_tile(const SchedLds &s, int t, int E, int NT, int bm_fixed) {
+__device__ __forceinline__ Tile decode_tile(const SchedLds &s, const int32_t *__restrict__ off_g,
+                                            int t, int E, int M_cap, int N, int bm_fixed) {
   int lo = 0, hi = E;  // start[lo] <= t < start[hi]
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
     if (s.start[mid] <= t) lo = mid; else hi = mid;
   }
-  Tile tl;
-  const int m = s.off[lo + 1] - s.off[lo];
+  const int r0 = clamp_off(off_g, lo, M_cap);
+  const int m = clamp_off(off_g, lo + 1, M_cap) - r0;
   const int b = bm_fixed ? bm_fixed : adaptive_bm(m);
+  const int bn = width_of(b);
+  const int NT = cdiv(N, bn);
+  const int n_mt = cdiv(m, b);
   const int local = t - s.start[lo];
-  const int mt = local / NT;
-  const int nt = local - mt * NT;
+  // groups of kGroupM M tiles; N outer, M inner inside a group
+  const int per_group = kGroupM * NT;
+  const int grp = local / per_group;
+  const int r = local - grp * per_group;
+  const int gm = min(kGroupM, n_mt - grp * kGroupM);  // M tiles in this group
+  const int nt = r / gm;
+  const int mt = grp * kGroupM + (r - nt * gm);
+  Tile tl;
   tl.expert = lo;
   tl.bm = b;
-  tl.row0 = s.off[lo] + mt * b;
+  tl.row0 = r0 + mt * b;
   tl.rows = min(b, m - mt * b);
-  tl.col0 = nt * kBN;
+  tl.col0 = nt * bn;
   return tl;
 }
 

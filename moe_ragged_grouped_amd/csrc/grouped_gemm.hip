@@ -5,9 +5,10 @@
 // tile-count prefix from the device-resident group offsets (gg_schedule.h),
 // then walks tile ids with a stride of the grid size, decoding each id into
 // {expert, row0, rows, col0, bm} and running that tile's K loop and epilogue
-// (gg_mainloop.h). The grid is sized from the occupancy of the kernel and the
-// CU count, capped by an upper bound of the tile count that the host can
-// derive from M_cap alone, so the launch never waits on the group sizes.
+// (gg_mainloop.h). Two workgroups run per CU whatever the mix of tile heights
+// in a launch. The grid is sized from the occupancy of the kernel and the CU
+// count, capped by an upper bound of the tile count that the host can derive
+// from M_cap alone, so the launch never waits on the group sizes.
 //
 // XCD-aware order: MI355X hands consecutive workgroup ids round-robin to its
 // 8 XCDs, each with a private L2. Workgroup b processes, in its i-th round,
@@ -15,7 +16,7 @@
 // run of the expert-major list; tiles that share an expert's A rows (same M
 // tile) or its weight columns (same N tile) then meet in the same L2.
 
-#include "../../include/grouped_gemm.h"
+#include "grouped_gemm.h"  // include/ (on the -I path)
 #include "gg_common.h"
 #include "gg_mainloop.h"
 #include "gg_schedule.h"
@@ -35,32 +36,70 @@ struct Params {
   int bm_fixed;  // 0 = per-expert choice
 };
 
-template <class Cfg>
-__device__ __forceinline__ void tile_body(const Params &p, const Tile &t, lds_u16 *lds) {
-  const uint16_t *Be = p.B + (size_t)t.expert * p.K * p.N;
-  run_tile<Cfg>(p.A, Be, p.C, t.row0, t.rows, t.col0, p.K, p.N, lds);
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+__device__ __forceinline__ const void *uniform_ptr(const void *p) {
+  const uint64_t b = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  return (const void *)(uintptr_t)(((uint64_t)hi << 32) | lo);
 }
 
-// MASK: bit 0 -> BM 16, bit 1 -> 32, bit 2 -> 64, bit 3 -> 128 compiled in.
+// One tile of one height: the tile's base pointers and sizes, then its K loop
+// and epilogue. Every input is wave-uniform; readfirstlane makes that visible
+// to the compiler, so these values live in scalar registers. In the kernel
+// that compiles in all five heights this is what keeps the largest height's
+// path within 256 VGPRs (two workgroups per CU) without spilling.
+template <class Cfg>
+__device__ __forceinline__ void tile_body(const uint16_t *A, const uint16_t *B, float *C, int K,
+                                          int N, int row0, int rows, int col0, int expert,
+                                          uint32_t lds_addr) {
+  lds_u16 *const lds = (lds_u16 *)(uintptr_t)uniform((int)lds_addr);
+  K = uniform(K);
+  N = uniform(N);
+  row0 = uniform(row0);
+  col0 = uniform(col0);
+  expert = uniform(expert);
+  TileArgs a;
+  a.A = (const uint16_t *)uniform_ptr(A) + (size_t)row0 * K;
+  a.B = (const uint16_t *)uniform_ptr(B) + (size_t)expert * K * N + col0;
+  a.C = (float *)uniform_ptr(C) + (size_t)row0 * N + col0;
+  a.rows = uniform(rows);
+  a.K = K;
+  a.N = N;
+  a.ncols = min(Cfg::BN, N - col0);
+  run_tile<Cfg>(a, lds);
+}
+
+template <class Cfg>
+__device__ __forceinline__ void tile_call(const Params &p, const Tile &t, uint32_t lds_addr) {
+  tile_body<Cfg>(p.A, p.B, p.C, p.K, p.N, t.row0, t.rows, t.col0, t.expert, lds_addr);
+}
+
+// MASK bit c compiles in tile height 16 << c (16, 32, 64, 128, 256). A launch
+// must compile in every height its schedule can produce.
 template <int MASK>
-__global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
+__global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(Params p) {
   extern __shared__ __attribute__((aligned(16))) uint16_t lds_dyn[];
   __shared__ SchedLds sched;
-  lds_u16 *const lds = (lds_u16 *)lds_dyn;
-  const int NT = cdiv(p.N, kBN);
-  const int total = build_schedule(sched, p.off, p.E, p.M_cap, NT, p.bm_fixed);
+  // the LDS base as a plain byte address pinned in a scalar register (the
+  // empty asm keeps the compiler from rematerialising it in vector registers)
+  uint32_t lds = (uint32_t)(uintptr_t)(lds_u16 *)lds_dyn;
+  asm volatile("" : "+s"(lds));
+  const int total = build_schedule(sched, p.off, p.E, p.M_cap, p.N, p.bm_fixed);
   const int G = gridDim.x;  // a multiple of kXcds
   const int b = blockIdx.x;
   const int slot = (b % kXcds) * (G / kXcds) + b / kXcds;
   for (int base = 0; base < total; base += G) {
     const int t = base + slot;
     if (t >= total) break;
-    const Tile tl = decode_tile(sched, t, p.E, NT, p.bm_fixed);
+    const Tile tl = decode_tile(sched, p.off, t, p.E, p.M_cap, p.N, p.bm_fixed);
     switch (tl.bm) {
-      case 16: if constexpr (MASK & 1) tile_body<Cfg16>(p, tl, lds); break;
-      case 32: if constexpr (MASK & 2) tile_body<Cfg32>(p, tl, lds); break;
-      case 64: if constexpr (MASK & 4) tile_body<Cfg64>(p, tl, lds); break;
-      default: if constexpr (MASK & 8) tile_body<Cfg128>(p, tl, lds); break;
+      case 16: if constexpr (MASK & 1) tile_call<Cfg16>(p, tl, lds); break;
+      case 32: if constexpr (MASK & 2) tile_call<Cfg32>(p, tl, lds); break;
+      case 64: if constexpr (MASK & 4) tile_call<Cfg64>(p, tl, lds); break;
+      case 128: if constexpr (MASK & 8) tile_call<Cfg128>(p, tl, lds); break;
+      default: if constexpr (MASK & 16) tile_call<Cfg256>(p, tl, lds); break;
     }
   }
 }
@@ -70,12 +109,11 @@ __global__ __launch_bounds__(kThreads) void tile_schedule_kernel(const int32_t *
                                                                  int32_t *tiles, int32_t *n_tiles,
                                                                  int max_tiles) {
   __shared__ SchedLds sched;
-  const int NT = cdiv(N, kBN);
-  const int total = build_schedule(sched, off, E, M_cap, NT, bm_fixed);
+  const int total = build_schedule(sched, off, E, M_cap, N, bm_fixed);
   if (threadIdx.x == 0) *n_tiles = total;
   const int lim = total < max_tiles ? total : max_tiles;
   for (int t = threadIdx.x; t < lim; t += kThreads) {
-    const Tile tl = decode_tile(sched, t, E, NT, bm_fixed);
+    const Tile tl = decode_tile(sched, off, t, E, M_cap, N, bm_fixed);
     int32_t *o = tiles + 5 * (size_t)t;
     o[0] = tl.expert;
     o[1] = tl.row0;
@@ -85,13 +123,17 @@ __global__ __launch_bounds__(kThreads) void tile_schedule_kernel(const int32_t *
   }
 }
 
+template <class C>
+constexpr int ring_bytes() { return C::LDS_BYTES; }
+
 template <int MASK>
 constexpr int lds_bytes() {
   int m = 0;
-  if (MASK & 1) m = m > Cfg16::LDS_BYTES ? m : Cfg16::LDS_BYTES;
-  if (MASK & 2) m = m > Cfg32::LDS_BYTES ? m : Cfg32::LDS_BYTES;
-  if (MASK & 4) m = m > Cfg64::LDS_BYTES ? m : Cfg64::LDS_BYTES;
-  if (MASK & 8) m = m > Cfg128::LDS_BYTES ? m : Cfg128::LDS_BYTES;
+  if (MASK & 1) m = m > ring_bytes<Cfg16>() ? m : ring_bytes<Cfg16>();
+  if (MASK & 2) m = m > ring_bytes<Cfg32>() ? m : ring_bytes<Cfg32>();
+  if (MASK & 4) m = m > ring_bytes<Cfg64>() ? m : ring_bytes<Cfg64>();
+  if (MASK & 8) m = m > ring_bytes<Cfg128>() ? m : ring_bytes<Cfg128>();
+  if (MASK & 16) m = m > ring_bytes<Cfg256>() ? m : ring_bytes<Cfg256>();
   return m;
 }
 
@@ -149,15 +191,16 @@ static gg_status_t check_sizes(const int32_t *off, int E, int N, int M_cap, int 
                                long long *tile_bound) {
   if (off == nullptr) return GG_ERR_INVALID_VALUE;
   if (E < 1 || N < 1 || M_cap < 0) return GG_ERR_INVALID_VALUE;
-  if (!(bm == 0 || bm == 16 || bm == 32 || bm == 64 || bm == 128)) return GG_ERR_INVALID_VALUE;
+  if (!(bm == 0 || bm == 16 || bm == 32 || bm == 64 || bm == 128 || bm == 256))
+    return GG_ERR_INVALID_VALUE;
   if (E > kMaxExperts) return GG_ERR_UNSUPPORTED;
   if (!aligned(off, 4)) return GG_ERR_MISALIGNED;
   if (N % 8 != 0) return GG_ERR_MISALIGNED;
   const long long hmin = bm ? bm : 16;
-  const long long nt = (N + kBN - 1) / kBN;
+  const long long nt = (N + 127) / 128;  // the narrowest tile width bounds the count
   const long long bound = ((long long)M_cap / hmin + E) * nt;
   // tile ids, rows + tile height and 5*tile indices must stay inside int32
-  if (bound > (1LL << 28) || (long long)M_cap + 128 > INT32_MAX) return GG_ERR_UNSUPPORTED;
+  if (bound > (1LL << 28) || (long long)M_cap + 256 > INT32_MAX) return GG_ERR_UNSUPPORTED;
   *tile_bound = bound;
   return GG_OK;
 }
@@ -185,7 +228,8 @@ extern "C" gg_status_t gg_grouped_gemm_bf16(const void *A, const void *B,
     case 32: return launch<2>(p, bound, s);
     case 64: return launch<4>(p, bound, s);
     case 128: return launch<8>(p, bound, s);
-    default: return launch<15>(p, bound, s);
+    case 256: return launch<16>(p, bound, s);
+    default: return launch<31>(p, bound, s);
   }
 }
 

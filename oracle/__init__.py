@@ -180,7 +180,7 @@ def algorithmic_bytes(sizes, K: int, N: int, c_bytes: int = 4, in_bytes: int = 2
 
 
 # Tile heights the HIP path supports, smallest first.
-BM_CHOICES = (16, 32, 64, 128)
+BM_CHOICES = (16, 32, 64, 128, 256)
 
 
 def adaptive_bm(sizes, choices=BM_CHOICES):

@@ -62,7 +62,7 @@ def _call(lib, **kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(A=0), 1), (dict(B=0), 1), (dict(C=0), 1), (dict(off=0), 1),
     (dict(E=0), 1), (dict(E=-3), 1), (dict(K=0), 1), (dict(N=0), 1), (dict(M_cap=-1), 1),
-    (dict(bm=8), 1), (dict(bm=256), 1), (dict(bm=48), 1),
+    (dict(bm=8), 1), (dict(bm=512), 1), (dict(bm=48), 1),
     (dict(A=24), 2), (dict(B=40), 2), (dict(C=8), 2), (dict(off=66), 2),
     (dict(K=12), 2), (dict(N=100), 2),
     (dict(E=1025), 3), (dict(M_cap=2**31 - 100), 3),

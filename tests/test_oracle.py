@@ -265,14 +265,18 @@ def test_compulsory_bytes_from_pages():
 
 def test_adaptive_bm_special_cases():
     # multiples of the largest height and very small experts are decided by padding alone
-    assert oracle.adaptive_bm([128, 256, 4096]) == [128, 128, 128]
+    assert oracle.adaptive_bm([256, 512, 4096]) == [256, 256, 256]
     assert oracle.adaptive_bm([1, 5, 16]) == [16, 16, 16]
     assert oracle.adaptive_bm([32]) == [32]
     assert oracle.adaptive_bm([0]) == [16]
-    # worked by hand: m=48 -> costs 16:3*80=240, 32:2*96=192, 64:1*128=128, 128:192 -> 64
+    # worked by hand: m=48 -> costs 16:3*80=240, 32:2*96=192, 64:1*128=128, 128:192, 256:320 -> 64
     assert oracle.adaptive_bm([48]) == [64]
-    # m=130 -> 16:9*80=720, 32:5*96=480, 64:3*128=384, 128:2*192=384 -> tie -> 128
-    assert oracle.adaptive_bm([130]) == [128]
+    # m=128 -> 64:2*128=256, 128:1*192=192, 256:320 -> 128
+    assert oracle.adaptive_bm([128]) == [128]
+    # m=130 -> 64:3*128=384, 128:2*192=384, 256:1*320=320 -> 256
+    assert oracle.adaptive_bm([130]) == [256]
+    # m=100 -> 64:2*128=256, 128:192, 256:320 -> 128
+    assert oracle.adaptive_bm([100]) == [128]
     # eta never below the uniform-BM=128 eta on the page skew law
     s = _golden_sizes("skew16k_page")
     assert oracle.eta(s, oracle.adaptive_bm(s)) >= oracle.eta(s, 128)

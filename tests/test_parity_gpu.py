@@ -20,7 +20,7 @@ from tests import parity
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
-BMS = [0, 16, 32, 64, 128]
+BMS = [0, 16, 32, 64, 128, 256]
 
 
 def _say(*a):
@@ -125,7 +125,28 @@ def test_repeat_is_deterministic(gg):
     assert (a == b).all()
 
 
-@pytest.mark.parametrize("sizes", [[3, 0, 17, 9], [0, 0, 1], [129, 0, 1000, 31, 16, 0, 2]])
+def _documented_order(tiles_page, N, width, group_m=8):
+    """The product kernel's walk order, from its documented rule: expert by
+    expert; inside an expert, M tiles in groups of up to 8, N outer and M inner
+    within a group."""
+    by_e = {}
+    for t in tiles_page:
+        by_e.setdefault(t[0], []).append(t)
+    out = []
+    for e in sorted(by_e):
+        ts = {(t[1], t[3]): t for t in by_e[e]}
+        rows0 = sorted({t[1] for t in by_e[e]})
+        cols0 = sorted({t[3] for t in by_e[e]})
+        for g in range(0, len(rows0), group_m):
+            grp = rows0[g:g + group_m]
+            for c in cols0:
+                for r in grp:
+                    out.append(ts[(r, c)])
+    return out
+
+
+@pytest.mark.parametrize("sizes", [[3, 0, 17, 9], [0, 0, 1], [129, 0, 1000, 31, 16, 0, 2],
+                                   [2500, 7, 0, 300]])
 @pytest.mark.parametrize("bm", BMS)
 @pytest.mark.parametrize("N", [256, 392])
 def test_tile_schedule_matches_oracle(gg, sizes, bm, N):
@@ -133,16 +154,21 @@ def test_tile_schedule_matches_oracle(gg, sizes, bm, N):
     M_cap = int(off[-1]) + 7
     _say("case schedule %s bm=%d N=%d" % (sizes, bm, N))
     tiles, n = gg.tile_schedule(torch.from_numpy(off).cuda(), N, M_cap, bm)
-    bms = oracle.adaptive_bm(sizes) if bm == 0 else bm
-    ref = oracle.tile_list(off, N, bms, gg.TILE_N)
+    hs = oracle.adaptive_bm(sizes) if bm == 0 else [bm] * len(sizes)
+    ws = [gg.TILE_WIDTH[h] for h in hs]
+    ref = oracle.tile_list(off, N, hs, ws)
     assert n == len(ref)
     got = [tuple(int(v) for v in r) for r in tiles.cpu().numpy()]
-    hs = bms if bm == 0 else [bm] * len(sizes)
-    assert got == [t + (hs[t[0]],) for t in ref]
+    want = [t + (hs[t[0]],) for t in ref]
+    # the set of descriptors is the page's, exactly
+    assert sorted(got) == sorted(want)
+    # the walk order is the documented one
+    assert got == [t + (hs[t[0]],) for t in _documented_order(ref, N, ws)]
 
 
 def test_tile_schedule_page_counts(gg):
-    # worklog section 3: 2,688 / 3,444 tiles at 128x128, balanced / skewed 16k
+    # worklog section 3: 2,688 / 3,444 tiles at 128x128, balanced / skewed 16k;
+    # 10,752 at BM=32 (BN=128), balanced 16k
     for sizes, bm, count in (([256] * 64, 128, 2688), (list(wl.page_skew_sizes(16384, 64, 1.2)), 128, 3444),
                              ([256] * 64, 32, 10752)):
         off = torch.from_numpy(wl.offsets_from_sizes(sizes)).cuda()

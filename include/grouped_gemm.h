@@ -43,12 +43,15 @@ typedef enum {
   GG_OK = 0,
   GG_ERR_INVALID_VALUE = 1, /* null pointer, non-positive size, bad bm        */
   GG_ERR_MISALIGNED = 2,    /* pointer not 16-byte aligned, K or N not 8k     */
-  GG_ERR_UNSUPPORTED = 3,   /* E > GG_MAX_EXPERTS or index range beyond int32 */
+  GG_ERR_UNSUPPORTED = 3,   /* E, K or N above its limit, or index range beyond int32 */
   GG_ERR_LAUNCH = 4         /* the HIP runtime refused the launch             */
 } gg_status_t;
 
 /* Largest number of groups one call accepts (the per-group tables live in LDS). */
 #define GG_MAX_EXPERTS 1024
+/* Largest K and N gg_grouped_gemm_bf16 accepts. */
+#define GG_MAX_K (1 << 22)
+#define GG_MAX_N (1 << 24)
 
 /*
  * gg_grouped_gemm_bf16 -- the grouped product (worklog section 2; glossary
@@ -64,6 +67,8 @@ typedef enum {
  *   C   fp32 [M_cap][N], row-major. Rows [0, M_tot) are overwritten with the
  *       product (not accumulated into); rows [M_tot, M_cap) are not touched.
  *   E in [1, GG_MAX_EXPERTS]; K >= 8 and N >= 8, both multiples of 8;
+ *   K <= GG_MAX_K and N <= GG_MAX_N (the kernels address a tile's A rows and
+ *   a K slice of B with 32-bit byte offsets);
  *   M_cap >= 0 (0: nothing is enqueued).
  *   bm  tile height: 16, 32, 64, 128 or 256 for every expert, or 0 to let
  *       the device choose per expert from its row count (the trade between
@@ -91,7 +96,7 @@ gg_status_t gg_grouped_gemm_bf16(const void *A, const void *B, const int32_t *gr
  * the worklog's; the order is expert by expert, and inside an expert the M
  * tiles are taken in groups of up to 8 with the N tile outer and the M tile
  * inner in each group (so consecutive tiles share a column slice of the
- * expert's weights). Tiles are 128 columns wide for every height. At most
+ * expert's weights). Tiles are 256 columns wide for every height. At most
  * max_tiles descriptors are written; *n_tiles (a device int32) receives the
  * full count even when it exceeds max_tiles.
  * Arguments E, N, M_cap, bm and the offsets rules are those of

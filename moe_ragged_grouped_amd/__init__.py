@@ -21,8 +21,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libmoe_ragged_grouped_amd.so")
 
 BM_CHOICES = (16, 32, 64, 128, 256)
-TILE_N = 128                      # narrowest tile width
-TILE_WIDTH = {16: 128, 32: 128, 64: 128, 128: 128, 256: 128}  # per tile height
+TILE_N = 256                      # tile width (every height)
+TILE_WIDTH = {h: TILE_N for h in BM_CHOICES}  # per tile height
 MAX_EXPERTS = 1024
 SYMBOLS = ("gg_grouped_gemm_bf16", "gg_tile_schedule", "gg_status_string")
 

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace gg {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
@@ -19,20 +21,50 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) uint16_t lds_u16;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 
-constexpr int kThreads = 256;  // four 64-lane waves per workgroup
+constexpr int kThreads = 512;  // eight 64-lane waves per workgroup
 constexpr int kWave = 64;
 
 __device__ __forceinline__ int cdiv(int a, int b) { return (a + b - 1) / b; }
 
-// Global-memory typed pointers: keep loads and stores global_* instructions
-// even where the compiler cannot see where a pointer came from (a generic
-// pointer would become flat_* accesses, which also count against the LDS
-// wait counter).
-typedef __attribute__((address_space(1))) const u32x4 gbl_cu32x4;
+__host__ __device__ constexpr int gcd(int a, int b) { return b == 0 ? a : gcd(b, a % b); }
+__host__ __device__ constexpr int lcm(int a, int b) { return a / gcd(a, b) * b; }
+
+// f(std::integral_constant<int, i>) for i = 0 .. N-1, unrolled at compile time.
+template <int N, int I = 0, class F>
+__device__ __forceinline__ void static_for(F &&f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, I + 1>(f);
+  }
+}
+
+// Global-memory typed pointer: keeps the epilogue stores global_*
+// instructions even where the compiler cannot see where a pointer came from
+// (a generic pointer would become flat_* accesses, which also count against
+// the LDS wait counter).
 typedef __attribute__((address_space(1))) f32x4 gbl_f32x4;
 
-// One 16-byte global load (global_load_dwordx4).
-__device__ __forceinline__ u32x4 ld_g16(const void *p) { return *(gbl_cu32x4 *)p; }
+// Raw buffer access (buffer_load_dwordx4 with a per-lane byte offset). The
+// resource holds a base address and a size in bytes; a lane whose offset
+// lies at or past the size reads zeros without touching memory. That range
+// check is the zero fill of padding rows, of K past its end and of columns
+// past N, with no branch and a 32-bit offset per lane instead of a 64-bit
+// address.
+typedef __amdgpu_buffer_rsrc_t buf_rsrc;
+constexpr int kBufWord3 = 0x00020000;  // gfx9-family raw buffer, no swizzle
+// A byte offset past every buffer this library describes (their sizes stay
+// at or below 2^31).
+constexpr uint32_t kOob = 0x80000000u;
+
+__device__ __forceinline__ buf_rsrc make_buf(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                           kBufWord3);
+}
+
+// One 16-byte load at base + voff + soff; zeros when the offset is out of range.
+__device__ __forceinline__ u32x4 ld_buf16(buf_rsrc r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+}
 
 // One 16-byte global store (global_store_dwordx4).
 __device__ __forceinline__ void st_g16(float *p, f32x4 v) { *(gbl_f32x4 *)p = v; }

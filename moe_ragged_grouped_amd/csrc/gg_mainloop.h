@@ -7,14 +7,17 @@
 // register-direct epilogue of section 4.1).
 //
 // MI355X mapping:
-//  * Two workgroups of four waves per CU (at most 256 registers per wave, at
-//    most 80 KiB of LDS per workgroup): for the weight-streaming shapes the
-//    bytes in flight per CU, not the tile shape, set the achieved HBM
-//    bandwidth, and a second resident workgroup doubles them.
+//  * One workgroup of eight waves per CU (two waves per SIMD, at most 256
+//    registers per wave; up to 141 KiB of LDS). Every tile is 256 columns
+//    wide, so a tile's A rows are fetched once per 256 output columns. What
+//    limits these kernels is how many bytes each CU's vector memory path
+//    (address unit and L1) keeps in flight against the L2/HBM latency, so the
+//    design minimises the bytes each CU must fetch (wide tiles, 128-byte row
+//    segments from 64-deep K slices) and keeps two slices of B in flight.
 //  * K runs in slices of BK: every thread moves 16-byte chunks global ->
-//    registers (global_load_dwordx4) for slice k+1 while the matrix cores work
-//    on slice k out of LDS, then writes them to the other of two LDS stages
-//    (ds_write_b128); one barrier per slice.
+//    registers (buffer_load_dwordx4) ahead of their use while the matrix
+//    cores work on slice k out of LDS, then writes them to the other of two
+//    LDS stages (ds_write_b128); one barrier per slice.
 //  * v_mfma_f32_16x16x32_bf16 computes C^T blocks: the first operand is a
 //    16 (n) x 32 (k) slice of B^T, the second a 32 (k) x 16 (m) slice of A^T.
 //    Both operands want 8 consecutive k per lane. A rows are K-contiguous in
@@ -34,10 +37,17 @@
 
 namespace gg {
 
-template <int BM_, int BK_, int WM_, int WN_>
+template <int BM_, int BK_, int WM_, int WN_, int AD_, int BD_, int NS_ = 2>
 struct TileCfg {
   static constexpr int BM = BM_, BN = width_of(BM_), BK = BK_, WM = WM_, WN = WN_;
-  static_assert(WM * WN == kThreads / kWave, "four waves per workgroup");
+  // K slices of A and of B held in registers ahead of the LDS stage
+  static constexpr int AD = AD_, BD = BD_;
+  // LDS stages: 2 = the next slice is written while the current one is read
+  // (one barrier per slice); 1 = write after a second barrier (half the LDS)
+  static constexpr int NS = NS_;
+  static_assert(NS == 1 || NS == 2, "LDS stages");
+  static_assert(WM * WN == kThreads / kWave, "one wave per wave tile");
+  static_assert(AD >= 1 && AD <= 3 && BD >= 1 && BD <= 4, "prefetch depths");
   static constexpr int WTM = BM / WM;  // rows of C per wave
   static constexpr int WTN = BN / WN;  // columns of C per wave
   static_assert(WTM % 16 == 0 && WTN % 16 == 0 && BK % 32 == 0, "16x16x32 blocks");
@@ -51,69 +61,111 @@ struct TileCfg {
   static constexpr int B_CHUNKS = BK * BN / 8;
   static constexpr int A_PER_T = (A_CHUNKS + kThreads - 1) / kThreads;
   static constexpr int B_PER_T = (B_CHUNKS + kThreads - 1) / kThreads;
-  static constexpr int LDS_BYTES = 2 * (A_STAGE + B_STAGE) * 2;
+  static constexpr int LDS_BYTES = NS * (A_STAGE + B_STAGE) * 2;
 };
 
-// Tile configurations per tile height (all 128 columns wide).
-using Cfg16 = TileCfg<16, 64, 1, 4>;    // wave tile 16 x 32
-using Cfg32 = TileCfg<32, 64, 1, 4>;    // wave tile 32 x 32
-using Cfg64 = TileCfg<64, 64, 1, 4>;    // wave tile 64 x 32
-using Cfg128 = TileCfg<128, 64, 2, 2>;  // wave tile 64 x 64
-using Cfg256 = TileCfg<256, 32, 2, 2>;  // wave tile 128 x 64 (32-deep slices fit 2 stages)
+// Tile configurations per tile height (all 256 columns wide; eight waves).
+using Cfg16 = TileCfg<16, 64, 1, 8, 1, 2>;    // wave tile 16 x 32
+using Cfg32 = TileCfg<32, 64, 1, 8, 1, 2>;    // wave tile 32 x 32
+using Cfg64 = TileCfg<64, 64, 1, 8, 1, 2>;    // wave tile 64 x 32
+using Cfg128 = TileCfg<128, 64, 2, 4, 1, 2>;  // wave tile 64 x 64
+using Cfg256 = TileCfg<256, 64, 2, 4, 1, 2>;  // wave tile 128 x 64
 
 struct TileArgs {
   const uint16_t *A;   // A rows of this tile: row r at A + r * K
   const uint16_t *B;   // B[e] + col0: element (k, n) at B + k * N + n
   float *C;            // C + row0 * N + col0
   int rows, K, N, ncols;  // ncols = valid columns in this tile (<= BN)
+  long long b_bytes;   // bytes from B to the end of B[e]: (K * N - col0) * 2
+  int tid;             // threadIdx.x, re-derived per tile (see tile_body)
 };
 
+// Register staging: the A chunks of the next AD K slices (slice s in
+// a[s % AD]) and the B chunks of the next BD slices (slice s in b[s % BD]).
 template <class C>
 struct Staging {
-  u32x4 a[C::A_PER_T];
-  u32x4 b[C::B_PER_T];
+  u32x4 a[C::AD][C::A_PER_T];
+  u32x4 b[C::BD][C::B_PER_T];
 };
 
-// Global -> registers for the K slice starting at k0. Out-of-range chunks
-// (rows past the tile's valid rows, K past the end, columns past N) are zero.
+// Per-thread load offsets of one tile. A thread's chunks of a K slice share
+// one K position (A) or one column position (B), because the chunk index
+// steps by the thread count, a multiple of the chunks per row.
 template <class C>
-__device__ __forceinline__ void load_slice(Staging<C> &st, const TileArgs &t, int k0) {
-  const int tid = threadIdx.x;
+struct Loads {
+  static_assert(kThreads % (C::BK / 8) == 0 && kThreads % (C::BN / 8) == 0, "chunk layout");
+  buf_rsrc a;                   // the tile's valid A rows: rows * K * 2 bytes
+  uint32_t a_off[C::A_PER_T];   // chunk i of this thread at k0 = 0, or kOob
+  uint32_t b_off[C::B_PER_T];   // chunk i of this thread inside a slice, or kOob
+  int a_k;                      // K position of this thread's A chunks in a slice
+};
+
+// Host limits keep every offset below 2^31: rows * K * 2 <= 256 * K * 2 and
+// BK * N * 2 <= 64 * N * 2.
+template <class C>
+__device__ __forceinline__ void init_loads(Loads<C> &L, const TileArgs &t) {
+  const int tid = t.tid;
+  L.a = make_buf(t.A, (uint32_t)t.rows * (uint32_t)t.K * 2u);
+  const int kc = tid % (C::BK / 8);
+  L.a_k = 8 * kc;
 #pragma unroll
   for (int i = 0; i < C::A_PER_T; ++i) {
     const int c = tid + i * kThreads;
-    const int r = c / (C::BK / 8), kc = c % (C::BK / 8);
-    const int k = k0 + 8 * kc;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (c < C::A_CHUNKS && r < t.rows && k < t.K) v = ld_g16(t.A + (size_t)r * t.K + k);
-    st.a[i] = v;
+    const uint32_t r = c / (C::BK / 8);
+    L.a_off[i] = c < C::A_CHUNKS ? (r * (uint32_t)t.K + 8u * kc) * 2u : kOob;
   }
+  const int n = 8 * (tid % (C::BN / 8));
 #pragma unroll
   for (int i = 0; i < C::B_PER_T; ++i) {
     const int c = tid + i * kThreads;
-    const int kr = c / (C::BN / 8), nc = c % (C::BN / 8);
-    const int k = k0 + kr, n = 8 * nc;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (c < C::B_CHUNKS && k < t.K && n < t.ncols) v = ld_g16(t.B + (size_t)k * t.N + n);
-    st.b[i] = v;
+    const uint32_t kr = c / (C::BN / 8);
+    L.b_off[i] = (c < C::B_CHUNKS && n < t.ncols) ? (kr * (uint32_t)t.N + n) * 2u : kOob;
   }
+}
+
+// Global -> registers for the K slice starting at k0. Rows past the tile's
+// valid rows, K past its end and columns past N read as zero: the A resource
+// ends at the last valid row, K-tail chunks of A get kOob, and the B resource
+// of a slice ends where B[e] ends (a slice at or past K has size 0).
+template <class C>
+__device__ __forceinline__ void load_a(u32x4 (&a)[C::A_PER_T], const Loads<C> &L,
+                                       const TileArgs &t, int k0) {
+  const bool kin = k0 + L.a_k < t.K;
+#pragma unroll
+  for (int i = 0; i < C::A_PER_T; ++i) a[i] = ld_buf16(L.a, kin ? L.a_off[i] : kOob, 2u * k0);
+}
+
+template <class C>
+__device__ __forceinline__ void load_b(u32x4 (&b)[C::B_PER_T], const Loads<C> &L,
+                                       const TileArgs &t, int k0) {
+  // bytes from the slice start to the end of B[e]; none for a slice past K
+  const long long rem = t.b_bytes - (long long)k0 * t.N * 2;
+  const uint32_t size = rem <= 0 ? 0u : (rem < kOob ? (uint32_t)rem : kOob);
+  const buf_rsrc r = make_buf(t.B + (size_t)k0 * t.N, size);
+#pragma unroll
+  for (int i = 0; i < C::B_PER_T; ++i) b[i] = ld_buf16(r, L.b_off[i], 0u);
 }
 
 // Registers -> one LDS stage.
 template <class C>
-__device__ __forceinline__ void store_slice(const Staging<C> &st, lds_u16 *As, lds_u16 *Bs) {
-  const int tid = threadIdx.x;
+__device__ __forceinline__ void store_a(const u32x4 (&a)[C::A_PER_T], lds_u16 *As, int tid) {
 #pragma unroll
   for (int i = 0; i < C::A_PER_T; ++i) {
     const int c = tid + i * kThreads;
     const int r = c / (C::BK / 8), kc = c % (C::BK / 8);
-    if (c < C::A_CHUNKS) *(lds_u32x4 *)(As + r * C::A_LD + 8 * kc) = st.a[i];
+    if (C::A_CHUNKS % kThreads == 0 || c < C::A_CHUNKS)
+      *(lds_u32x4 *)(As + r * C::A_LD + 8 * kc) = a[i];
   }
+}
+
+template <class C>
+__device__ __forceinline__ void store_b(const u32x4 (&b)[C::B_PER_T], lds_u16 *Bs, int tid) {
 #pragma unroll
   for (int i = 0; i < C::B_PER_T; ++i) {
     const int c = tid + i * kThreads;
     const int kr = c / (C::BN / 8), nc = c % (C::BN / 8);
-    if (c < C::B_CHUNKS) *(lds_u32x4 *)(Bs + kr * C::B_LD + 8 * nc) = st.b[i];
+    if (C::B_CHUNKS % kThreads == 0 || c < C::B_CHUNKS)
+      *(lds_u32x4 *)(Bs + kr * C::B_LD + 8 * nc) = b[i];
   }
 }
 
@@ -122,8 +174,7 @@ __device__ __forceinline__ void store_slice(const Staging<C> &st, lds_u16 *As, l
 // block at a time, which keeps a tall wave tile's register footprint small.
 template <class C>
 __device__ __forceinline__ void mma_stage(f32x4 (&acc)[C::NI][C::MI], const lds_u16 *As,
-                                          const lds_u16 *Bs, int wm0, int wn0) {
-  const int lane = threadIdx.x % kWave;
+                                          const lds_u16 *Bs, int wm0, int wn0, int lane) {
   const int g = lane / 16, s = lane % 16;
 #pragma unroll
   for (int ks = 0; ks < C::BK / 32; ++ks) {
@@ -144,6 +195,9 @@ __device__ __forceinline__ void mma_stage(f32x4 (&acc)[C::NI][C::MI], const lds_
       for (int ni = 0; ni < C::NI; ++ni)
         acc[ni][mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x[ni], y, acc[ni][mi], 0, 0, 0);
     }
+    // one K step at a time: hoisting the next step's fragments above this
+    // step's products would add their registers on top of the accumulators
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -152,8 +206,9 @@ __device__ __forceinline__ void mma_stage(f32x4 (&acc)[C::NI][C::MI], const lds_
 template <class C>
 __device__ __forceinline__ void run_tile(const TileArgs &t, lds_u16 *lds) {
   lds_u16 *const As0 = lds;                       // stage s: As0 + s * A_STAGE
-  lds_u16 *const Bs0 = lds + 2 * C::A_STAGE;      // stage s: Bs0 + s * B_STAGE
-  const int wave = threadIdx.x / kWave;
+  lds_u16 *const Bs0 = lds + C::NS * C::A_STAGE;  // stage s: Bs0 + s * B_STAGE
+  const int wave = __builtin_amdgcn_readfirstlane(t.tid / kWave);
+  const int lane = t.tid % kWave;
   const int wm0 = (wave / C::WN) * C::WTM;
   const int wn0 = (wave % C::WN) * C::WTN;
 
@@ -163,22 +218,59 @@ __device__ __forceinline__ void run_tile(const TileArgs &t, lds_u16 *lds) {
 #pragma unroll
     for (int mi = 0; mi < C::MI; ++mi) acc[ni][mi] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // Slices of A and B are loaded AD and BD slices ahead of their use. Tiles
+  // that share A rows or B columns run side by side and request the same
+  // lines at about the same time, so most loads wait for HBM, not L2. The
+  // steady-state loop (every slice but the last) is unrolled so that each
+  // staging buffer and each LDS stage has a fixed name, and its body is free
+  // of branches: slices past K are still "loaded" (all lanes out of range,
+  // so zeros and no memory traffic). The compiler's in-order vmcnt
+  // accounting then stores slice s+1 while the loads of later slices stay in
+  // flight.
   const int KT = cdiv(t.K, C::BK);
+  Loads<C> L;
+  init_loads<C>(L, t);
   Staging<C> st;
-  load_slice<C>(st, t, 0);
-  store_slice<C>(st, As0, Bs0);
+  static_for<(C::AD > C::BD ? C::AD : C::BD)>([&](auto jc) {
+    constexpr int j = decltype(jc)::value;
+    if constexpr (j < C::AD) load_a<C>(st.a[j], L, t, j * C::BK);
+    if constexpr (j < C::BD) load_b<C>(st.b[j], L, t, j * C::BK);
+  });
+  store_a<C>(st.a[0], As0, t.tid);
+  store_b<C>(st.b[0], Bs0, t.tid);
   __syncthreads();
-  for (int kt = 0; kt < KT; ++kt) {
-    const bool more = kt + 1 < KT;
-    const int cur = kt & 1, nxt = cur ^ 1;
-    if (more) load_slice<C>(st, t, (kt + 1) * C::BK);
-    mma_stage<C>(acc, As0 + cur * C::A_STAGE, Bs0 + cur * C::B_STAGE, wm0, wn0);
-    if (more) store_slice<C>(st, As0 + nxt * C::A_STAGE, Bs0 + nxt * C::B_STAGE);
+
+  // one steady-state step: slice kt (kt % U == j) from its stage, slice kt + 1
+  // into the other
+  auto step = [&](auto jc, int kt) {
+    constexpr int j = decltype(jc)::value;
+    constexpr int cur = j % C::NS, nxt = (j + 1) % C::NS;
+    load_a<C>(st.a[j % C::AD], L, t, (kt + C::AD) * C::BK);
+    load_b<C>(st.b[j % C::BD], L, t, (kt + C::BD) * C::BK);
+    // keep the loads ahead of the matrix work (the scheduler would otherwise
+    // sink them next to their LDS stores and expose their latency)
+    __builtin_amdgcn_sched_barrier(0);
+    mma_stage<C>(acc, As0 + cur * C::A_STAGE, Bs0 + cur * C::B_STAGE, wm0, wn0, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (C::NS == 1) __syncthreads();  // every wave is done reading the stage
+    store_a<C>(st.a[(j + 1) % C::AD], As0 + nxt * C::A_STAGE, t.tid);
+    store_b<C>(st.b[(j + 1) % C::BD], Bs0 + nxt * C::B_STAGE, t.tid);
     __syncthreads();
-  }
+  };
+  // unroll factor: a multiple of AD, BD and 2
+  constexpr int U = lcm(lcm(C::AD, C::BD), 2);
+  int kt0 = 0;
+  for (; kt0 + U <= KT - 1; kt0 += U)
+    static_for<U>([&](auto jc) { step(jc, kt0 + decltype(jc)::value); });
+  static_for<U - 1>([&](auto jc) {
+    if (kt0 + decltype(jc)::value < KT - 1) step(jc, kt0 + decltype(jc)::value);
+  });
+  // the last slice sits in stage (KT - 1) % NS
+  const int last = (KT - 1) % C::NS;
+  mma_stage<C>(acc, As0 + last * C::A_STAGE, Bs0 + last * C::B_STAGE, wm0, wn0, lane);
+  __syncthreads();
 
   // epilogue: lane holds C[m][n..n+3] for m = s, n = 4g within each 16x16 block
-  const int lane = threadIdx.x % kWave;
   const int g = lane / 16, s = lane % 16;
 #pragma unroll
   for (int mi = 0; mi < C::MI; ++mi) {

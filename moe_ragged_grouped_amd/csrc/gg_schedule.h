@@ -28,11 +28,12 @@ namespace gg {
 constexpr int kMaxExperts = 1024;  // the tile prefix lives in LDS
 constexpr int kGroupM = 8;         // M tiles per group in the within-expert order
 
-// Tile heights this library runs, smallest first; every tile is 128 columns
-// wide.
+// Tile heights this library runs, smallest first; every tile is kTileN
+// columns wide.
 constexpr int kNumHeights = 5;
+constexpr int kTileN = 256;
 __host__ __device__ constexpr int height_of(int cls) { return 16 << cls; }
-__host__ __device__ constexpr int width_of(int) { return 128; }
+__host__ __device__ constexpr int width_of(int) { return kTileN; }
 
 // Per-expert tile height when the caller leaves the choice to the device.
 // Minimises ceil(m/BM) * (BM + 64) over BM in {16, 32, 64, 128, 256}: the
@@ -79,7 +80,7 @@ __device__ __forceinline__ int clamp_off(const int32_t *off_g, int e, int M_cap)
 __device__ inline int build_schedule(SchedLds &s, const int32_t *__restrict__ off_g, int E,
                                      int M_cap, int N, int bm_fixed) {
   const int tid = threadIdx.x;
-  // each thread owns a run of consecutive experts (E <= 1024 -> at most 4)
+  // each thread owns a run of consecutive experts (E <= 1024 -> at most 2)
   constexpr int kRun = kMaxExperts / kThreads;
   const int e0 = tid * kRun;
   int cnt[kRun];

@@ -5,10 +5,10 @@
 // tile-count prefix from the device-resident group offsets (gg_schedule.h),
 // then walks tile ids with a stride of the grid size, decoding each id into
 // {expert, row0, rows, col0, bm} and running that tile's K loop and epilogue
-// (gg_mainloop.h). Two workgroups run per CU whatever the mix of tile heights
-// in a launch. The grid is sized from the occupancy of the kernel and the CU
-// count, capped by an upper bound of the tile count that the host can derive
-// from M_cap alone, so the launch never waits on the group sizes.
+// (gg_mainloop.h). The grid is sized from the occupancy of the kernel (one
+// eight-wave workgroup per CU once the tallest tiles are compiled in) and the
+// CU count, capped by an upper bound of the tile count that the host can
+// derive from M_cap alone, so the launch never waits on the group sizes.
 //
 // XCD-aware order: MI355X hands consecutive workgroup ids round-robin to its
 // 8 XCDs, each with a private L2. Workgroup b processes, in its i-th round,
@@ -26,6 +26,8 @@
 namespace gg {
 
 constexpr int kXcds = 8;
+constexpr int kMaxK = 1 << 22;
+constexpr int kMaxN = 1 << 24;
 
 struct Params {
   const uint16_t *A;
@@ -49,7 +51,7 @@ __device__ __forceinline__ const void *uniform_ptr(const void *p) {
 // and epilogue. Every input is wave-uniform; readfirstlane makes that visible
 // to the compiler, so these values live in scalar registers. In the kernel
 // that compiles in all five heights this is what keeps the largest height's
-// path within 256 VGPRs (two workgroups per CU) without spilling.
+// path within 256 VGPRs (two waves per SIMD) without spilling.
 template <class Cfg>
 __device__ __forceinline__ void tile_body(const uint16_t *A, const uint16_t *B, float *C, int K,
                                           int N, int row0, int rows, int col0, int expert,
@@ -68,6 +70,13 @@ __device__ __forceinline__ void tile_body(const uint16_t *A, const uint16_t *B, 
   a.K = K;
   a.N = N;
   a.ncols = min(Cfg::BN, N - col0);
+  a.b_bytes = ((long long)K * N - col0) * 2;
+  // The per-thread index arithmetic of a tile depends only on threadIdx.x; an
+  // opaque copy per tile keeps the compiler from hoisting all of it out of
+  // the persistent loop, where it would stay live (and spill) across tiles.
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  a.tid = tid;
   run_tile<Cfg>(a, lds);
 }
 
@@ -79,7 +88,7 @@ __device__ __forceinline__ void tile_call(const Params &p, const Tile &t, uint32
 // MASK bit c compiles in tile height 16 << c (16, 32, 64, 128, 256). A launch
 // must compile in every height its schedule can produce.
 template <int MASK>
-__global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(Params p) {
+__global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(Params p) {
   extern __shared__ __attribute__((aligned(16))) uint16_t lds_dyn[];
   __shared__ SchedLds sched;
   // the LDS base as a plain byte address pinned in a scalar register (the
@@ -197,7 +206,7 @@ static gg_status_t check_sizes(const int32_t *off, int E, int N, int M_cap, int 
   if (!aligned(off, 4)) return GG_ERR_MISALIGNED;
   if (N % 8 != 0) return GG_ERR_MISALIGNED;
   const long long hmin = bm ? bm : 16;
-  const long long nt = (N + 127) / 128;  // the narrowest tile width bounds the count
+  const long long nt = (N + kTileN - 1) / kTileN;
   const long long bound = ((long long)M_cap / hmin + E) * nt;
   // tile ids, rows + tile height and 5*tile indices must stay inside int32
   if (bound > (1LL << 28) || (long long)M_cap + 256 > INT32_MAX) return GG_ERR_UNSUPPORTED;
@@ -218,6 +227,9 @@ extern "C" gg_status_t gg_grouped_gemm_bf16(const void *A, const void *B,
   if (st != GG_OK) return st;
   if (A == nullptr || B == nullptr || C == nullptr || K < 1) return GG_ERR_INVALID_VALUE;
   if (K % 8 != 0) return GG_ERR_MISALIGNED;
+  // 32-bit buffer offsets: a tile's A rows (256 * K * 2 bytes) and a K slice
+  // of B (64 * N * 2 bytes) must stay below 2^31 bytes
+  if (K > kMaxK || N > kMaxN) return GG_ERR_UNSUPPORTED;
   if (!aligned(A, 16) || !aligned(B, 16) || !aligned(C, 16)) return GG_ERR_MISALIGNED;
   if (M_cap == 0 || bound == 0) return GG_OK;
   Params p{static_cast<const uint16_t *>(A), static_cast<const uint16_t *>(B), group_offsets, C,
@@ -253,7 +265,7 @@ extern "C" const char *gg_status_string(gg_status_t status) {
     case GG_OK: return "success";
     case GG_ERR_INVALID_VALUE: return "invalid argument (null pointer, size or tile height)";
     case GG_ERR_MISALIGNED: return "misaligned pointer, or K or N not a multiple of 8";
-    case GG_ERR_UNSUPPORTED: return "unsupported problem (too many experts or rows)";
+    case GG_ERR_UNSUPPORTED: return "unsupported problem (too many experts or rows, K or N too large)";
     case GG_ERR_LAUNCH: return "kernel launch failed";
   }
   return "unknown status";

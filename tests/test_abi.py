@@ -66,6 +66,7 @@ def _call(lib, **kw):
     (dict(A=24), 2), (dict(B=40), 2), (dict(C=8), 2), (dict(off=66), 2),
     (dict(K=12), 2), (dict(N=100), 2),
     (dict(E=1025), 3), (dict(M_cap=2**31 - 100), 3),
+    (dict(K=2**22 + 8), 3), (dict(N=2**24 + 8), 3),
 ])
 def test_host_checks(lib, kw, status):
     assert _call(lib, **kw) == status

@@ -1,8 +1,9 @@
 """Build checks for the gfx950 kernels (no GPU): every kernel compiles without
 register spills or scratch memory, and fits the residency the launch assumes.
 
-The kernels sit close to the 256-register budget of two resident workgroups per
-CU, so a source change that tips one into spilling would slow it down silently;
+The kernels sit close to the 256-register budget of two waves per SIMD (one
+eight-wave workgroup per CU), so a source change that tips one into spilling
+would slow it down silently;
 this test makes that loud. The figures come from the compiler's
 kernel-resource-usage remarks for our own gfx950 build.
 """
@@ -50,8 +51,8 @@ def test_no_spills_no_scratch(resources):
         assert r.get("ScratchSize [bytes/lane]", 0) == 0, (name, r)
 
 
-def test_two_workgroups_per_cu(resources):
-    # four waves per workgroup and two workgroups per CU: two waves per SIMD,
+def test_two_waves_per_simd(resources):
+    # eight waves per workgroup and one workgroup per CU: two waves per SIMD,
     # so at most 256 registers (VGPR + AGPR) per wave
     for name, r in resources.items():
         if "grouped_gemm_kernel" in name:

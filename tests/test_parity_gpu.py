@@ -1,8 +1,8 @@
 """HIP path vs the CPU oracle, element by element (needs an MI355X).
 
-Small problems are compared whole: they span several 128-column tiles, several
-64-deep K slices with a partial last slice, experts smaller than one tile,
-experts spanning many tiles and empty experts. The full-size workloads are
+Small problems are compared whole: they span several 256-column tiles with a
+ragged last one, several 64-deep K slices with a partial last slice, experts
+smaller than one tile, experts spanning many tiles and empty experts. The full-size workloads are
 compared on sampled entries the oracle computes one dot product at a time,
 plus properties that hold at any size (every routed row written and finite,
 rows past the last group untouched).
@@ -73,6 +73,14 @@ def test_tiny(gg, bm):
 def test_ragged_multi_tile(gg, bm):
     w = wl.make_workload(E=6, K=328, N=392, sizes=[0, 1, 17, 130, 0, 300], seed=21, M_cap=470)
     _full_compare(gg, w, bm, "ragged")
+
+
+@pytest.mark.parametrize("bm", BMS)
+def test_ragged_wide(gg, bm):
+    # three full 256-column tiles and an 8-column tail; K = 200 ends inside a
+    # 64-deep slice; the largest expert spans three 256-row tiles
+    w = wl.make_workload(E=4, K=200, N=776, sizes=[300, 0, 45, 517], seed=27, M_cap=870)
+    _full_compare(gg, w, bm, "ragged-wide")
 
 
 @pytest.mark.parametrize("bm", BMS)
@@ -167,13 +175,18 @@ def test_tile_schedule_matches_oracle(gg, sizes, bm, N):
 
 
 def test_tile_schedule_page_counts(gg):
-    # worklog section 3: 2,688 / 3,444 tiles at 128x128, balanced / skewed 16k;
-    # 10,752 at BM=32 (BN=128), balanced 16k
-    for sizes, bm, count in (([256] * 64, 128, 2688), (list(wl.page_skew_sizes(16384, 64, 1.2)), 128, 3444),
-                             ([256] * 64, 32, 10752)):
+    # worklog section 3 counts 2,688 / 3,444 tiles of 128x128 for the balanced /
+    # skewed 16k problems and 10,752 at BM=32 (BN=128); the oracle's tile list
+    # reproduces those figures (CPU tests). The device tiles are 256 wide, so
+    # the same problems give exactly half as many M-by-N tiles plus one extra
+    # column of half-empty tiles per M tile: N = 2688 = 10.5 * 256.
+    for sizes, bm, count128 in (([256] * 64, 128, 2688),
+                                (list(wl.page_skew_sizes(16384, 64, 1.2)), 128, 3444),
+                                ([256] * 64, 32, 10752)):
+        m_tiles = count128 // 21  # 2688 / 128 = 21 column tiles at BN = 128
         off = torch.from_numpy(wl.offsets_from_sizes(sizes)).cuda()
         _, n = gg.tile_schedule(off, 2688, 16384, bm, max_tiles=0)
-        assert n == count
+        assert n == m_tiles * 11 == len(oracle.tile_list(wl.offsets_from_sizes(sizes), 2688, bm, gg.TILE_N))
 
 
 def test_malformed_offsets_stay_in_bounds(gg):
@@ -221,7 +234,7 @@ def _samples(w, rng, n_random=3000):
         r0, r1 = int(off[e]), int(off[e + 1])
         if r1 > r0:
             for r in {r0, r1 - 1, (r0 + r1) // 2}:
-                for c in (0, 1, 127, 128, w.N - 1, int(rng.integers(0, w.N))):
+                for c in (0, 1, 255, 256, w.N - 1, int(rng.integers(0, w.N))):
                     rows.append(r)
                     cols.append(c)
     rows += list(rng.integers(0, w.M_tot, size=n_random))
@@ -250,10 +263,11 @@ def test_full_size_sampled(gg, name):
     assert (d <= parity.ELEM * s).all(), "worst ratio %.3e" % float(np.max(d / s))
     rel = np.linalg.norm(got - c) / np.linalg.norm(c)
     assert rel <= parity.REL_FRO
-    # one whole 128x128 output block of the largest expert, entry by entry
+    # the first (up to) 128 rows of the largest expert across the whole second
+    # 256-column tile, entry by entry
     e = int(np.argmax(w.sizes))
     r0 = int(w.offsets[e])
     nr = min(128, int(w.sizes[e]))
-    rr, cc = np.meshgrid(np.arange(r0, r0 + nr), np.arange(128, 256), indexing="ij")
+    rr, cc = np.meshgrid(np.arange(r0, r0 + nr), np.arange(256, 512), indexing="ij")
     c2, s2 = oracle.grouped_gemm_entries(w.A, w.B, w.offsets, rr.ravel(), cc.ravel())
     parity.check(out[rr.ravel(), cc.ravel()], c2, s2, name + " block")

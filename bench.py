@@ -10,7 +10,7 @@ routed rows, K=6144, N=4096).
 Prints one JSON line:
   value      useful TFLOP/s = 2*M_tot*K*N / (time per step)
   roofline   the kernel against its bound: algorithmic bytes (A once, B once
-             per expert with rows, C once as fp32) per launch over the average
+             per expert with rows, C once) per launch over the average
              launch time (HIP events on the launch stream), vs 8 TB/s HBM3E;
              or useful flops vs 2.5 PFLOP/s dense bf16 when the workload's
              arithmetic intensity is above the ridge point. "traffic" is the
@@ -19,7 +19,10 @@ Prints one JSON line:
              sources, else null.
   cpu_baseline  the CPU oracle timed on a bounded sample of the same workload.
 
-    python bench.py [--steps K] [--warmup W] [--config decode] [--bm 0]
+    python bench.py [--steps K] [--warmup W] [--config decode] [--bm 0] [--out fp32|bf16]
+
+--out bf16 times the bf16-output entry point (C rounded to bf16 in the
+epilogue); its algorithmic bytes count C at 2 bytes per element.
 """
 
 import argparse
@@ -59,13 +62,14 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(config, bm):
+def measured_traffic(config, bm, out="fp32"):
     """HBM bytes per launch from the committed counter summary, if still current."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     try:
-        rec = json.load(open(path)).get("%s/bm%d" % (config, bm))
+        key = "%s/bm%d" % (config, bm) + ("" if out == "fp32" else "/" + out)
+        rec = json.load(open(path)).get(key)
     except (OSError, ValueError):
         return None
     if not rec or rec.get("kernel_source_hash") != kernel_source_hash():
@@ -115,6 +119,8 @@ def main():
     ap.add_argument("--ramp-ms", type=float, default=300.0,
                     help="untimed launches for at least this long before the warmup steps, so "
                          "the GPU clocks have left their idle state when timing starts")
+    ap.add_argument("--out", default="fp32", choices=("fp32", "bf16"),
+                    help="element type of C (bf16: rounded in the epilogue)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (for counter calibration)")
@@ -151,7 +157,8 @@ def main():
     A = torch.from_numpy(w.A.view(np.int16)).to(dev).view(torch.bfloat16)
     B = torch.from_numpy(w.B.view(np.int16)).to(dev).view(torch.bfloat16)
     off = torch.from_numpy(w.offsets).to(dev)
-    C = torch.empty((w.M_cap, w.N), dtype=torch.float32, device=dev)
+    c_dtype = torch.float32 if args.out == "fp32" else torch.bfloat16
+    C = torch.empty((w.M_cap, w.N), dtype=c_dtype, device=dev)
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream(dev)
@@ -188,11 +195,13 @@ def main():
     launch_s = ev_s / args.steps                # average launch on the stream
 
     useful = 2.0 * w.M_tot * w.K * w.N
-    alg_bytes = 2 * w.M_tot * w.K + 2 * w.K * w.N * int((w.sizes > 0).sum()) + 4 * w.M_tot * w.N
+    c_bytes = 4 if args.out == "fp32" else 2
+    alg_bytes = (2 * w.M_tot * w.K + 2 * w.K * w.N * int((w.sizes > 0).sum())
+                 + c_bytes * w.M_tot * w.N)
     intensity = useful / alg_bytes
     hbm_gbs = alg_bytes / launch_s / 1e9
     tflops_launch = useful / launch_s / 1e12
-    traffic = measured_traffic(args.config, args.bm)
+    traffic = measured_traffic(args.config, args.bm, args.out)
     if intensity < RIDGE:
         roof = {"bound": "hbm", "achieved": round(hbm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(hbm_gbs / HBM_PEAK_GBS, 4), "traffic": traffic}
@@ -224,7 +233,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded normal draws rounded to bf16, no dataset)",
         "config": {"workload": DESCRIPTIONS[args.config], "name": args.config, "E": w.E, "K": w.K,
-                   "N": w.N, "M_tot": w.M_tot, "bm": args.bm or "per-expert", "out_dtype": "fp32"},
+                   "N": w.N, "M_tot": w.M_tot, "bm": args.bm or "per-expert", "out_dtype": args.out},
         "hbm_gbs": round(hbm_gbs, 1),
         "hbm_frac": round(hbm_gbs / HBM_PEAK_GBS, 4),
         "mfma_frac": round(tflops_launch / MFMA_BF16_PEAK_TFLOPS, 4),

@@ -84,6 +84,23 @@ gg_status_t gg_grouped_gemm_bf16(const void *A, const void *B, const int32_t *gr
                                  int32_t bm, void *stream);
 
 /*
+ * gg_grouped_gemm_bf16_bf16out -- the same product with bf16 output C.
+ *
+ * The worklog's compulsory-traffic model (section 2.1, about 474 MB at 16k)
+ * counts C as 2-byte values. Every argument and rule is that of
+ * gg_grouped_gemm_bf16 except C:
+ *   C   bf16 [M_cap][N], row-major, 16-byte aligned. Each element is the fp32
+ *       matrix-core result rounded once to the nearest bf16 (ties to even),
+ *       so it is within half a bf16 unit (2^-9 relative) of the fp32 result
+ *       gg_grouped_gemm_bf16 returns for the same inputs, and equal to that
+ *       result rounded to bf16.
+ */
+gg_status_t gg_grouped_gemm_bf16_bf16out(const void *A, const void *B,
+                                         const int32_t *group_offsets, void *C, int32_t E,
+                                         int32_t K, int32_t N, int32_t M_cap, int32_t bm,
+                                         void *stream);
+
+/*
  * gg_tile_schedule -- the flat tile list the product kernel consumes,
  * written out (worklog section 2: one descriptor per output tile of one
  * expert, expert-major order, tiles stopping at expert boundaries, empty

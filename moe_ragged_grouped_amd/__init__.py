@@ -24,7 +24,8 @@ BM_CHOICES = (16, 32, 64, 128, 256)
 TILE_N = 256                      # tile width (every height)
 TILE_WIDTH = {h: TILE_N for h in BM_CHOICES}  # per tile height
 MAX_EXPERTS = 1024
-SYMBOLS = ("gg_grouped_gemm_bf16", "gg_tile_schedule", "gg_status_string")
+SYMBOLS = ("gg_grouped_gemm_bf16", "gg_grouped_gemm_bf16_bf16out", "gg_tile_schedule",
+           "gg_status_string")
 
 _lib = None
 
@@ -48,6 +49,8 @@ def load_library():
         vp, i32 = ctypes.c_void_p, ctypes.c_int32
         lib.gg_grouped_gemm_bf16.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
         lib.gg_grouped_gemm_bf16.restype = ctypes.c_int
+        lib.gg_grouped_gemm_bf16_bf16out.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
+        lib.gg_grouped_gemm_bf16_bf16out.restype = ctypes.c_int
         lib.gg_tile_schedule.argtypes = [vp, i32, i32, i32, i32, vp, vp, i32, vp]
         lib.gg_tile_schedule.restype = ctypes.c_int
         lib.gg_status_string.argtypes = [ctypes.c_int]
@@ -69,12 +72,14 @@ def _stream_handle(device, stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def grouped_gemm(A, B, offsets, out=None, bm: int = 0, stream=None):
+def grouped_gemm(A, B, offsets, out=None, bm: int = 0, stream=None, out_dtype=None):
     """C[off[e]:off[e+1]] = A[off[e]:off[e+1]] @ B[e] for every expert e, in one launch.
 
     A: bf16 [M_cap, K]; B: bf16 [E, K, N]; offsets: int32 [E+1] (device);
-    out: optional fp32 [M_cap, N]; bm: 0 (per-expert choice on the device)
-    or 16/32/64/128/256. Rows of ``out`` at or past offsets[E] are left as they
+    out: optional fp32 or bf16 [M_cap, N] (out_dtype, default fp32, when out
+    is not given); bm: 0 (per-expert choice on the device) or
+    16/32/64/128/256. A bf16 ``out`` receives the fp32 result rounded to
+    nearest even. Rows of ``out`` at or past offsets[E] are left as they
     were. Enqueued on ``stream`` (default: torch's current stream).
     """
     import torch
@@ -95,12 +100,17 @@ def grouped_gemm(A, B, offsets, out=None, bm: int = 0, stream=None):
         raise ValueError("shape mismatch: A %s, B %s, offsets %s" % (tuple(A.shape), tuple(B.shape),
                                                                       tuple(offsets.shape)))
     if out is None:
-        out = torch.empty((M_cap, N), dtype=torch.float32, device=A.device)
-    elif out.dtype != torch.float32 or tuple(out.shape) != (M_cap, N) or not out.is_contiguous():
-        raise ValueError("out must be a contiguous fp32 [M_cap, N] tensor")
-    st = lib.gg_grouped_gemm_bf16(A.data_ptr(), B.data_ptr(), offsets.data_ptr(), out.data_ptr(),
-                                  E, K, N, M_cap, int(bm), _stream_handle(A.device, stream))
-    _check(st, "gg_grouped_gemm_bf16")
+        dt = torch.float32 if out_dtype is None else out_dtype
+        if dt not in (torch.float32, torch.bfloat16):
+            raise TypeError("out_dtype must be torch.float32 or torch.bfloat16")
+        out = torch.empty((M_cap, N), dtype=dt, device=A.device)
+    elif (out.dtype not in (torch.float32, torch.bfloat16) or tuple(out.shape) != (M_cap, N)
+          or not out.is_contiguous() or (out_dtype is not None and out.dtype != out_dtype)):
+        raise ValueError("out must be a contiguous fp32 or bf16 [M_cap, N] tensor")
+    fn = lib.gg_grouped_gemm_bf16 if out.dtype == torch.float32 else lib.gg_grouped_gemm_bf16_bf16out
+    st = fn(A.data_ptr(), B.data_ptr(), offsets.data_ptr(), out.data_ptr(), E, K, N, M_cap, int(bm),
+            _stream_handle(A.device, stream))
+    _check(st, fn.__name__)
     return out
 
 

@@ -69,6 +69,18 @@ __device__ __forceinline__ u32x4 ld_buf16(buf_rsrc r, uint32_t voff, uint32_t so
 // One 16-byte global store (global_store_dwordx4).
 __device__ __forceinline__ void st_g16(float *p, f32x4 v) { *(gbl_f32x4 *)p = v; }
 
+// Output element types of the epilogue.
+enum class Out { F32, BF16 };
+
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+typedef __attribute__((address_space(1))) bf16x4 gbl_bf16x4;
+
+// Four fp32 values rounded to bf16 (v_cvt_pk_bf16_f32, round to nearest even)
+// and stored as one 8-byte global store.
+__device__ __forceinline__ void st_g8_bf16(uint16_t *p, f32x4 v) {
+  *(gbl_bf16x4 *)p = __builtin_convertvector(v, bf16x4);
+}
+
 // Transposing LDS read of a 4 (rows) x 16 (16-bit columns) block per 16-lane
 // group (ds_read_b64_tr_b16). Lane 16g + s supplies the address of 4
 // consecutive 16-bit values; the instruction returns to lane 16g + i the

@@ -28,8 +28,9 @@
 //    per clock per CU against 172 for ds_read_b128, so tall wave tiles (fewer
 //    B fragments per flop) are preferred.
 //  * The accumulator layout of C^T gives every lane 4 consecutive columns of
-//    one row of C, so the epilogue is one 16-byte store per lane per block,
-//    straight from registers with a per-lane row guard.
+//    one row of C, so the epilogue is one 16-byte store (fp32 C) or one 8-byte
+//    store (bf16 C) per lane per block, straight from registers with a
+//    per-lane row guard.
 #pragma once
 
 #include "gg_common.h"
@@ -74,7 +75,7 @@ using Cfg256 = TileCfg<256, 64, 2, 4, 1, 2>;  // wave tile 128 x 64
 struct TileArgs {
   const uint16_t *A;   // A rows of this tile: row r at A + r * K
   const uint16_t *B;   // B[e] + col0: element (k, n) at B + k * N + n
-  float *C;            // C + row0 * N + col0
+  void *C;             // C + row0 * N + col0, fp32 or bf16 elements
   int rows, K, N, ncols;  // ncols = valid columns in this tile (<= BN)
   long long b_bytes;   // bytes from B to the end of B[e]: (K * N - col0) * 2
   int tid;             // threadIdx.x, re-derived per tile (see tile_body)
@@ -202,8 +203,10 @@ __device__ __forceinline__ void mma_stage(f32x4 (&acc)[C::NI][C::MI], const lds_
 }
 
 // Full K loop and epilogue for one tile. lds must hold C::LDS_BYTES. Ends with
-// a workgroup barrier, so the next tile may refill the stages at once.
-template <class C>
+// a workgroup barrier, so the next tile may refill the stages at once. O is
+// the element type of C: fp32 (the accumulators as they are) or bf16 (rounded
+// to nearest even in the epilogue).
+template <class C, Out O>
 __device__ __forceinline__ void run_tile(const TileArgs &t, lds_u16 *lds) {
   lds_u16 *const As0 = lds;                       // stage s: As0 + s * A_STAGE
   lds_u16 *const Bs0 = lds + C::NS * C::A_STAGE;  // stage s: Bs0 + s * B_STAGE
@@ -276,11 +279,15 @@ __device__ __forceinline__ void run_tile(const TileArgs &t, lds_u16 *lds) {
   for (int mi = 0; mi < C::MI; ++mi) {
     const int m = wm0 + mi * 16 + s;
     if (m < t.rows) {
-      float *crow = t.C + (size_t)m * t.N;
 #pragma unroll
       for (int ni = 0; ni < C::NI; ++ni) {
         const int n = wn0 + ni * 16 + 4 * g;
-        if (n < t.ncols) st_g16(crow + n, acc[ni][mi]);
+        if (n < t.ncols) {
+          if constexpr (O == Out::F32)
+            st_g16((float *)t.C + (size_t)m * t.N + n, acc[ni][mi]);
+          else
+            st_g8_bf16((uint16_t *)t.C + (size_t)m * t.N + n, acc[ni][mi]);
+        }
       }
     }
   }

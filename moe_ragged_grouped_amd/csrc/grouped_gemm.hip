@@ -33,7 +33,7 @@ struct Params {
   const uint16_t *A;
   const uint16_t *B;
   const int32_t *off;
-  float *C;
+  void *C;  // fp32 or bf16 [M_cap][N]
   int E, K, N, M_cap;
   int bm_fixed;  // 0 = per-expert choice
 };
@@ -52,8 +52,8 @@ __device__ __forceinline__ const void *uniform_ptr(const void *p) {
 // to the compiler, so these values live in scalar registers. In the kernel
 // that compiles in all five heights this is what keeps the largest height's
 // path within 256 VGPRs (two waves per SIMD) without spilling.
-template <class Cfg>
-__device__ __forceinline__ void tile_body(const uint16_t *A, const uint16_t *B, float *C, int K,
+template <class Cfg, Out O>
+__device__ __forceinline__ void tile_body(const uint16_t *A, const uint16_t *B, void *C, int K,
                                           int N, int row0, int rows, int col0, int expert,
                                           uint32_t lds_addr) {
   lds_u16 *const lds = (lds_u16 *)(uintptr_t)uniform((int)lds_addr);
@@ -65,7 +65,8 @@ __device__ __forceinline__ void tile_body(const uint16_t *A, const uint16_t *B, 
   TileArgs a;
   a.A = (const uint16_t *)uniform_ptr(A) + (size_t)row0 * K;
   a.B = (const uint16_t *)uniform_ptr(B) + (size_t)expert * K * N + col0;
-  a.C = (float *)uniform_ptr(C) + (size_t)row0 * N + col0;
+  constexpr size_t kOutBytes = O == Out::F32 ? 4 : 2;
+  a.C = (char *)uniform_ptr(C) + ((size_t)row0 * N + col0) * kOutBytes;
   a.rows = uniform(rows);
   a.K = K;
   a.N = N;
@@ -77,17 +78,18 @@ __device__ __forceinline__ void tile_body(const uint16_t *A, const uint16_t *B, 
   int tid = threadIdx.x;
   asm volatile("" : "+v"(tid));
   a.tid = tid;
-  run_tile<Cfg>(a, lds);
+  run_tile<Cfg, O>(a, lds);
 }
 
-template <class Cfg>
+template <class Cfg, Out O>
 __device__ __forceinline__ void tile_call(const Params &p, const Tile &t, uint32_t lds_addr) {
-  tile_body<Cfg>(p.A, p.B, p.C, p.K, p.N, t.row0, t.rows, t.col0, t.expert, lds_addr);
+  tile_body<Cfg, O>(p.A, p.B, p.C, p.K, p.N, t.row0, t.rows, t.col0, t.expert, lds_addr);
 }
 
 // MASK bit c compiles in tile height 16 << c (16, 32, 64, 128, 256). A launch
-// must compile in every height its schedule can produce.
-template <int MASK>
+// must compile in every height its schedule can produce. O is the element
+// type of C.
+template <int MASK, Out O>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(Params p) {
   extern __shared__ __attribute__((aligned(16))) uint16_t lds_dyn[];
   __shared__ SchedLds sched;
@@ -104,11 +106,11 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(Params p) {
     if (t >= total) break;
     const Tile tl = decode_tile(sched, p.off, t, p.E, p.M_cap, p.N, p.bm_fixed);
     switch (tl.bm) {
-      case 16: if constexpr (MASK & 1) tile_call<Cfg16>(p, tl, lds); break;
-      case 32: if constexpr (MASK & 2) tile_call<Cfg32>(p, tl, lds); break;
-      case 64: if constexpr (MASK & 4) tile_call<Cfg64>(p, tl, lds); break;
-      case 128: if constexpr (MASK & 8) tile_call<Cfg128>(p, tl, lds); break;
-      default: if constexpr (MASK & 16) tile_call<Cfg256>(p, tl, lds); break;
+      case 16: if constexpr (MASK & 1) tile_call<Cfg16, O>(p, tl, lds); break;
+      case 32: if constexpr (MASK & 2) tile_call<Cfg32, O>(p, tl, lds); break;
+      case 64: if constexpr (MASK & 4) tile_call<Cfg64, O>(p, tl, lds); break;
+      case 128: if constexpr (MASK & 8) tile_call<Cfg128, O>(p, tl, lds); break;
+      default: if constexpr (MASK & 16) tile_call<Cfg256, O>(p, tl, lds); break;
     }
   }
 }
@@ -154,7 +156,7 @@ struct LaunchInfo {
 
 constexpr int kMaxDevices = 64;
 
-template <int MASK>
+template <int MASK, Out O>
 static LaunchInfo launch_info(int dev) {
   static LaunchInfo cache[kMaxDevices];
   static std::once_flag once[kMaxDevices];
@@ -164,11 +166,11 @@ static LaunchInfo launch_info(int dev) {
     const int lds = lds_bytes<MASK>();
     li.err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (li.err == hipSuccess)
-      li.err = hipFuncSetAttribute((const void *)grouped_gemm_kernel<MASK>,
+      li.err = hipFuncSetAttribute((const void *)grouped_gemm_kernel<MASK, O>,
                                    hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (li.err == hipSuccess)
       li.err = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &per_cu, (const void *)grouped_gemm_kernel<MASK>, kThreads, lds);
+          &per_cu, (const void *)grouped_gemm_kernel<MASK, O>, kThreads, lds);
     if (li.err == hipSuccess) {
       if (per_cu < 1) per_cu = 1;
       li.grid = cus * per_cu;
@@ -180,15 +182,15 @@ static LaunchInfo launch_info(int dev) {
   return cache[dev];
 }
 
-template <int MASK>
+template <int MASK, Out O>
 static gg_status_t launch(const Params &p, long long tile_bound, hipStream_t stream) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return GG_ERR_LAUNCH;
-  const LaunchInfo li = launch_info<MASK>(dev);
+  const LaunchInfo li = launch_info<MASK, O>(dev);
   if (li.err != hipSuccess) return GG_ERR_LAUNCH;
   long long g = tile_bound < li.grid ? tile_bound : li.grid;
   g = (g + kXcds - 1) / kXcds * kXcds;  // keep a multiple of the XCD count
-  hipLaunchKernelGGL(grouped_gemm_kernel<MASK>, dim3((unsigned)g), dim3(kThreads),
+  hipLaunchKernelGGL((grouped_gemm_kernel<MASK, O>), dim3((unsigned)g), dim3(kThreads),
                      lds_bytes<MASK>(), stream, p);
   return hipGetLastError() == hipSuccess ? GG_OK : GG_ERR_LAUNCH;
 }
@@ -214,14 +216,11 @@ static gg_status_t check_sizes(const int32_t *off, int E, int N, int M_cap, int 
   return GG_OK;
 }
 
-}  // namespace gg
-
-using namespace gg;
-
-extern "C" gg_status_t gg_grouped_gemm_bf16(const void *A, const void *B,
-                                            const int32_t *group_offsets, float *C, int32_t E,
-                                            int32_t K, int32_t N, int32_t M_cap, int32_t bm,
-                                            void *stream) {
+// The product with C of element type O: argument checks, then one launch.
+template <Out O>
+static gg_status_t grouped_gemm(const void *A, const void *B, const int32_t *group_offsets,
+                                void *C, int32_t E, int32_t K, int32_t N, int32_t M_cap,
+                                int32_t bm, void *stream) {
   long long bound = 0;
   gg_status_t st = check_sizes(group_offsets, E, N, M_cap, bm, &bound);
   if (st != GG_OK) return st;
@@ -236,13 +235,31 @@ extern "C" gg_status_t gg_grouped_gemm_bf16(const void *A, const void *B,
            E, K, N, M_cap, bm};
   hipStream_t s = static_cast<hipStream_t>(stream);
   switch (bm) {
-    case 16: return launch<1>(p, bound, s);
-    case 32: return launch<2>(p, bound, s);
-    case 64: return launch<4>(p, bound, s);
-    case 128: return launch<8>(p, bound, s);
-    case 256: return launch<16>(p, bound, s);
-    default: return launch<31>(p, bound, s);
+    case 16: return launch<1, O>(p, bound, s);
+    case 32: return launch<2, O>(p, bound, s);
+    case 64: return launch<4, O>(p, bound, s);
+    case 128: return launch<8, O>(p, bound, s);
+    case 256: return launch<16, O>(p, bound, s);
+    default: return launch<31, O>(p, bound, s);
   }
+}
+
+}  // namespace gg
+
+using namespace gg;
+
+extern "C" gg_status_t gg_grouped_gemm_bf16(const void *A, const void *B,
+                                            const int32_t *group_offsets, float *C, int32_t E,
+                                            int32_t K, int32_t N, int32_t M_cap, int32_t bm,
+                                            void *stream) {
+  return grouped_gemm<Out::F32>(A, B, group_offsets, C, E, K, N, M_cap, bm, stream);
+}
+
+extern "C" gg_status_t gg_grouped_gemm_bf16_bf16out(const void *A, const void *B,
+                                                    const int32_t *group_offsets, void *C,
+                                                    int32_t E, int32_t K, int32_t N,
+                                                    int32_t M_cap, int32_t bm, void *stream) {
+  return grouped_gemm<Out::BF16>(A, B, group_offsets, C, E, K, N, M_cap, bm, stream);
 }
 
 extern "C" gg_status_t gg_tile_schedule(const int32_t *group_offsets, int32_t E, int32_t N,

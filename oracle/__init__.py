@@ -29,6 +29,11 @@ Contents
   (A once, B once per expert that has rows, C once).
 * ``adaptive_bm``: the per-expert tile-height rule of the HIP path, written
   from its stated definition (see the function).
+* ``round_to_bf16``: binary64 -> bfloat16 rounding to nearest, ties to even,
+  written from the IEEE-754 definition of the format (8 significant bits,
+  fp32's exponent range). It turns the fp64 reference into the bf16 values a
+  bf16-output product may return (the worklog's traffic model, section 2.1,
+  counts C in 2-byte values).
 
 Every function is pinned by ``tests/test_oracle.py`` (brute force, library
 products, closed forms, the pages' printed figures); none is unpinned.
@@ -208,4 +213,26 @@ def adaptive_bm(sizes, choices=BM_CHOICES):
             if best_cost is None or cost <= best_cost:
                 best, best_cost = b, cost
         out.append(best)
+    return out
+
+
+def round_to_bf16(x):
+    """Round binary64 values to bfloat16 (nearest, ties to even); float64 out.
+
+    bfloat16 keeps fp32's 8 exponent bits and 8 significant bits. A finite
+    x with 2^(e-1) <= |x| < 2^e (numpy.frexp) has a unit in the last place of
+    2^(e-8) while it is normal (|x| >= 2^-126); below that the spacing stays
+    2^-133 (subnormals). Scaling by a power of two is exact in binary64, so
+    x / ulp is exact and numpy's round (half to even) applies the tie rule.
+    A result at or above 2^128 overflows to infinity.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    out = np.zeros_like(x)
+    nz = (x != 0) & np.isfinite(x)
+    _, e = np.frexp(x[nz])
+    ulp = np.ldexp(1.0, np.maximum(e - 8, -133))
+    r = np.round(x[nz] / ulp) * ulp
+    r[np.abs(r) >= 2.0 ** 128] = np.inf * np.sign(r[np.abs(r) >= 2.0 ** 128])
+    out[nz] = r
+    out[~np.isfinite(x)] = x[~np.isfinite(x)]
     return out

@@ -51,11 +51,11 @@ def test_status_strings(lib):
 GOOD = dict(A=16, B=32, off=64, C=128, E=4, K=256, N=256, M_cap=29, bm=0)
 
 
-def _call(lib, **kw):
+def _call(lib, fn="gg_grouped_gemm_bf16", **kw):
     a = dict(GOOD)
     a.update(kw)
     # fake but aligned device addresses: every call below is rejected on the host
-    return lib.gg_grouped_gemm_bf16(a["A"], a["B"], a["off"], a["C"], a["E"], a["K"], a["N"],
+    return getattr(lib, fn)(a["A"], a["B"], a["off"], a["C"], a["E"], a["K"], a["N"],
                                     a["M_cap"], a["bm"], None)
 
 
@@ -68,8 +68,9 @@ def _call(lib, **kw):
     (dict(E=1025), 3), (dict(M_cap=2**31 - 100), 3),
     (dict(K=2**22 + 8), 3), (dict(N=2**24 + 8), 3),
 ])
-def test_host_checks(lib, kw, status):
-    assert _call(lib, **kw) == status
+@pytest.mark.parametrize("fn", ["gg_grouped_gemm_bf16", "gg_grouped_gemm_bf16_bf16out"])
+def test_host_checks(lib, kw, status, fn):
+    assert _call(lib, fn, **kw) == status
 
 
 def test_empty_problem_enqueues_nothing(lib):

@@ -280,3 +280,40 @@ def test_adaptive_bm_special_cases():
     # eta never below the uniform-BM=128 eta on the page skew law
     s = _golden_sizes("skew16k_page")
     assert oracle.eta(s, oracle.adaptive_bm(s)) >= oracle.eta(s, 128)
+
+
+def test_round_to_bf16_definition_cases():
+    # values of the format map to themselves; ties go to the even significand;
+    # anything past a tie goes up; the subnormal spacing is 2^-133; the largest
+    # finite bf16 is (2 - 2^-7) * 2^127 and a value that rounds past it is inf
+    cases = [
+        (1.0, 1.0), (1.0 + 2 ** -7, 1.0 + 2 ** -7), (-3.5, -3.5), (2.0 ** -126, 2.0 ** -126),
+        (1.0 + 2 ** -8, 1.0),                          # tie, 1.0 is even
+        (1.0 + 3 * 2 ** -8, 1.0 + 2 ** -6),            # tie, 1 + 2^-6 is even
+        (1.0 + 2 ** -8 + 2 ** -30, 1.0 + 2 ** -7),     # just past the tie
+        (-(1.0 + 2 ** -8 + 2 ** -30), -(1.0 + 2 ** -7)),
+        (255.0, 255.0), (257.0, 256.0), (259.0, 260.0),  # integers: spacing 2 above 256
+        (2.0 ** -130 + 2.0 ** -134, 2.0 ** -130),      # subnormal tie to even
+        (3 * 2.0 ** -134, 2.0 ** -132),                # 1.5 units of 2^-133: tie to 2
+        ((2 - 2 ** -7) * 2.0 ** 127, (2 - 2 ** -7) * 2.0 ** 127),
+        ((2 - 2 ** -9) * 2.0 ** 127, math.inf),
+        (0.0, 0.0),
+    ]
+    x = np.array([c[0] for c in cases])
+    want = np.array([c[1] for c in cases])
+    assert (oracle.round_to_bf16(x) == want).all(), (oracle.round_to_bf16(x), want)
+
+
+def test_round_to_bf16_matches_torch_on_fp32_values():
+    # on binary32 inputs the binary64 rounding must agree with torch's fp32 ->
+    # bf16 conversion (a library routine; no double rounding is possible since
+    # the inputs are exact in both formats)
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(11)
+    x = np.concatenate([rng.standard_normal(200000) * s for s in (1e-3, 1.0, 37.0, 1e5)])
+    x32 = x.astype(np.float32)
+    want = torch.from_numpy(x32).to(torch.bfloat16).to(torch.float64).numpy()
+    assert (oracle.round_to_bf16(x32.astype(np.float64)) == want).all()
+    # monotone nondecreasing
+    xs = np.sort(x)
+    assert (np.diff(oracle.round_to_bf16(xs)) >= 0).all()

@@ -271,3 +271,79 @@ def test_full_size_sampled(gg, name):
     rr, cc = np.meshgrid(np.arange(r0, r0 + nr), np.arange(256, 512), indexing="ij")
     c2, s2 = oracle.grouped_gemm_entries(w.A, w.B, w.offsets, rr.ravel(), cc.ravel())
     parity.check(out[rr.ravel(), cc.ravel()], c2, s2, name + " block")
+
+
+# ---- bf16 output C --------------------------------------------------------------
+
+def _run_bf16(gg, w, bm):
+    A, B, off = _dev(w)
+    C = torch.full((w.M_cap, w.N), float("nan"), dtype=torch.bfloat16, device="cuda:0")
+    gg.grouped_gemm(A, B, off, out=C, bm=bm)
+    torch.cuda.synchronize()
+    return C.float().cpu().numpy().astype(np.float64)
+
+
+def _full_compare_bf16(gg, w, bm, what):
+    _say("case bf16-out %s E=%d K=%d N=%d M_tot=%d bm=%d" % (what, w.E, w.K, w.N, w.M_tot, bm))
+    got = _run_bf16(gg, w, bm)
+    ref, s, _ = oracle.grouped_gemm(w.A, w.B, w.offsets)
+    m = w.M_tot
+    parity.check_bf16(got[:m], ref[:m], s[:m], what)
+    assert np.isnan(got[m:]).all(), "%s: rows past the last group were written" % what
+
+
+@pytest.mark.parametrize("bm", BMS)
+def test_bf16_out_tiny(gg, bm):
+    _full_compare_bf16(gg, wl.make_workload("tiny"), bm, "tiny")
+
+
+@pytest.mark.parametrize("bm", BMS)
+def test_bf16_out_ragged_wide(gg, bm):
+    w = wl.make_workload(E=4, K=200, N=776, sizes=[300, 0, 45, 517], seed=27, M_cap=870)
+    _full_compare_bf16(gg, w, bm, "ragged-wide")
+
+
+@pytest.mark.parametrize("bm", [0, 16, 256])
+def test_bf16_out_integer_inputs_exact(gg, bm):
+    # integer inputs: the fp32 result is exact, so the bf16 output must be the
+    # oracle's value rounded to bf16, exactly (|c| reaches 350, past 256 where
+    # bf16 integers become spaced 2 apart, so some entries do round)
+    w = wl.make_workload(E=5, K=512, N=264, sizes=[5, 0, 40, 129, 16], seed=22, values="int")
+    _say("case bf16-out int-exact bm=%d" % bm)
+    got = _run_bf16(gg, w, bm)
+    ref, _, _ = oracle.grouped_gemm(w.A, w.B, w.offsets, want_s=False)
+    m = w.M_tot
+    assert (oracle.round_to_bf16(ref[:m]) != ref[:m]).any()
+    assert (got[:m] == oracle.round_to_bf16(ref[:m])).all()
+
+
+@pytest.mark.parametrize("bm", [0, 64])
+def test_bf16_out_is_fp32_out_rounded(gg, bm):
+    # the two entry points share the main loop: the bf16 result is the fp32
+    # result rounded to nearest even, bit for bit
+    w = wl.make_workload(E=6, K=328, N=392, sizes=[0, 1, 17, 130, 0, 300], seed=21, M_cap=470)
+    _say("case bf16-out vs fp32-out bm=%d" % bm)
+    A, B, off = _dev(w)
+    c32 = gg.grouped_gemm(A, B, off, bm=bm)
+    c16 = gg.grouped_gemm(A, B, off, bm=bm, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    m = w.M_tot
+    assert torch.equal(c32[:m].cpu().to(torch.bfloat16).view(torch.int16), c16[:m].cpu().view(torch.int16))
+
+
+def test_bf16_out_full_size_sampled(gg):
+    w = _full("uniform16k")
+    guard = 16
+    dev = torch.device("cuda:0")
+    A, B, off = _dev(w)
+    Cbig = torch.full((w.M_cap + guard, w.N), float("nan"), dtype=torch.bfloat16, device=dev)
+    _say("case bf16-out full uniform16k")
+    gg.grouped_gemm(A, B, off, out=Cbig[: w.M_cap], bm=0)
+    torch.cuda.synchronize()
+    out = Cbig.float().cpu().numpy().astype(np.float64)
+    assert np.isfinite(out[: w.M_tot]).all()
+    assert np.isnan(out[w.M_cap:]).all()
+    rng = np.random.default_rng(8)
+    rows, cols = _samples(w, rng)
+    c, s = oracle.grouped_gemm_entries(w.A, w.B, w.offsets, rows, cols)
+    parity.check_bf16(out[rows, cols], c, s, "uniform16k bf16 sampled")

@@ -121,6 +121,8 @@ def main():
                          "the GPU clocks have left their idle state when timing starts")
     ap.add_argument("--out", default="fp32", choices=("fp32", "bf16"),
                     help="element type of C (bf16: rounded in the epilogue)")
+    ap.add_argument("--gather", action="store_true",
+                    help="time the gather/scatter entry point (A rows and C rows by index)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (for counter calibration)")
@@ -159,10 +161,26 @@ def main():
     off = torch.from_numpy(w.offsets).to(dev)
     c_dtype = torch.float32 if args.out == "fp32" else torch.bfloat16
     C = torch.empty((w.M_cap, w.N), dtype=c_dtype, device=dev)
+    if args.gather:
+        # rows reached by index: X holds the routed rows in a seeded random
+        # (token) order, grouped row r reads X[perm[r]] and is written back to
+        # C[perm[r]] (top-1 routing: permute in, GEMM, permute out)
+        if args.out != "fp32":
+            raise SystemExit("--gather times the fp32-output gather entry point")
+        perm_np = np.random.default_rng(w.seed + 500).permutation(w.M_cap).astype(np.int32)
+        X = torch.empty_like(A)
+        X[torch.from_numpy(perm_np).long().to(dev)] = A
+        perm = torch.from_numpy(perm_np).to(dev)
+
+    def step():
+        if args.gather:
+            gg.grouped_gemm_gather(X, perm, B, off, dst_rows=perm, out=C, bm=args.bm)
+        else:
+            gg.grouped_gemm(A, B, off, out=C, bm=args.bm)
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream(dev)
-    gg.grouped_gemm(A, B, off, out=C, bm=args.bm)  # correctness launch position of the protocol
+    step()  # correctness launch position of the protocol
     # Clock ramp: after the seconds of host-side input generation the GPU sits
     # at idle clocks, and a few milliseconds of warmup launches do not bring
     # it back up (a 10-launch warmup times the 16k shape about 18% slow).
@@ -170,13 +188,13 @@ def main():
     t_ramp = time.perf_counter()
     while (time.perf_counter() - t_ramp) * 1e3 < args.ramp_ms:
         for _ in range(20):
-            gg.grouped_gemm(A, B, off, out=C, bm=args.bm)
+            step()
         ramp_launches += 20
         torch.cuda.synchronize()
     print("bench: clock ramp %d launches, warmup %d launches" % (ramp_launches, args.warmup),
           file=sys.stderr, flush=True)
     for _ in range(args.warmup):
-        gg.grouped_gemm(A, B, off, out=C, bm=args.bm)
+        step()
     torch.cuda.synchronize()
 
     print("bench: timing %d launches" % args.steps, file=sys.stderr, flush=True)
@@ -186,7 +204,7 @@ def main():
     t0 = time.perf_counter()
     ev0.record(stream)
     for _ in range(args.steps):
-        gg.grouped_gemm(A, B, off, out=C, bm=args.bm)
+        step()
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -197,11 +215,11 @@ def main():
     useful = 2.0 * w.M_tot * w.K * w.N
     c_bytes = 4 if args.out == "fp32" else 2
     alg_bytes = (2 * w.M_tot * w.K + 2 * w.K * w.N * int((w.sizes > 0).sum())
-                 + c_bytes * w.M_tot * w.N)
+                 + c_bytes * w.M_tot * w.N + (8 * w.M_tot if args.gather else 0))
     intensity = useful / alg_bytes
     hbm_gbs = alg_bytes / launch_s / 1e9
     tflops_launch = useful / launch_s / 1e12
-    traffic = measured_traffic(args.config, args.bm, args.out)
+    traffic = None if args.gather else measured_traffic(args.config, args.bm, args.out)
     if intensity < RIDGE:
         roof = {"bound": "hbm", "achieved": round(hbm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(hbm_gbs / HBM_PEAK_GBS, 4), "traffic": traffic}
@@ -233,7 +251,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded normal draws rounded to bf16, no dataset)",
         "config": {"workload": DESCRIPTIONS[args.config], "name": args.config, "E": w.E, "K": w.K,
-                   "N": w.N, "M_tot": w.M_tot, "bm": args.bm or "per-expert", "out_dtype": args.out},
+                   "N": w.N, "M_tot": w.M_tot, "bm": args.bm or "per-expert", "out_dtype": args.out,
+                   "rows": "gathered/scattered by index" if args.gather else "grouped"},
         "hbm_gbs": round(hbm_gbs, 1),
         "hbm_frac": round(hbm_gbs / HBM_PEAK_GBS, 4),
         "mfma_frac": round(tflops_launch / MFMA_BF16_PEAK_TFLOPS, 4),

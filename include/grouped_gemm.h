@@ -101,6 +101,36 @@ gg_status_t gg_grouped_gemm_bf16_bf16out(const void *A, const void *B,
                                          void *stream);
 
 /*
+ * gg_grouped_gemm_bf16_gather -- the product with the expert grouping done by
+ * index instead of by copying rows (the worklog's "What I am measuring" puts
+ * the token permutation on either side of the grouped GEMM; here it is folded
+ * into the A loads and the C stores).
+ *
+ *   X         bf16 [n_src][K], row-major, 16-byte aligned: the unpermuted
+ *             rows (e.g. token activations).
+ *   src_rows  int32 [M_cap] on the device, 4-byte aligned: grouped row r
+ *             (expert e owns grouped rows off[e] .. off[e+1]-1, exactly as
+ *             in gg_grouped_gemm_bf16) reads its A row from X[src_rows[r]].
+ *             An index outside [0, n_src) reads a row of zeros. Entries at
+ *             or past off[E] are never read.
+ *   dst_rows  int32 [M_cap] on the device, 4-byte aligned, or NULL: grouped
+ *             row r is written to C row dst_rows[r]; an index outside
+ *             [0, M_cap) is not written. With NULL, grouped row r is written
+ *             to C row r, as in gg_grouped_gemm_bf16. Two grouped rows that
+ *             name the same C row race (either result may land).
+ *   C         fp32 [M_cap][N], row-major; rows no grouped row names are not
+ *             touched.
+ *   n_src >= 0 and n_src * K * 2 <= 2^31 (GG_ERR_UNSUPPORTED otherwise).
+ * The other arguments, rules and the accuracy are those of
+ * gg_grouped_gemm_bf16. The result equals gg_grouped_gemm_bf16 applied to
+ * A = X[src_rows] followed by C[dst_rows[r]] = C_grouped[r].
+ */
+gg_status_t gg_grouped_gemm_bf16_gather(const void *X, int32_t n_src, const int32_t *src_rows,
+                                        const void *B, const int32_t *group_offsets, float *C,
+                                        const int32_t *dst_rows, int32_t E, int32_t K, int32_t N,
+                                        int32_t M_cap, int32_t bm, void *stream);
+
+/*
  * gg_tile_schedule -- the flat tile list the product kernel consumes,
  * written out (worklog section 2: one descriptor per output tile of one
  * expert, expert-major order, tiles stopping at expert boundaries, empty

@@ -14,7 +14,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["grouped_gemm", "tile_schedule", "library_path", "load_library", "GroupedGemmError",
+__all__ = ["grouped_gemm", "grouped_gemm_gather", "tile_schedule", "library_path", "load_library", "GroupedGemmError",
            "BM_CHOICES", "TILE_N", "TILE_WIDTH", "MAX_EXPERTS", "SYMBOLS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -24,8 +24,8 @@ BM_CHOICES = (16, 32, 64, 128, 256)
 TILE_N = 256                      # tile width (every height)
 TILE_WIDTH = {h: TILE_N for h in BM_CHOICES}  # per tile height
 MAX_EXPERTS = 1024
-SYMBOLS = ("gg_grouped_gemm_bf16", "gg_grouped_gemm_bf16_bf16out", "gg_tile_schedule",
-           "gg_status_string")
+SYMBOLS = ("gg_grouped_gemm_bf16", "gg_grouped_gemm_bf16_bf16out", "gg_grouped_gemm_bf16_gather",
+           "gg_tile_schedule", "gg_status_string")
 
 _lib = None
 
@@ -51,6 +51,9 @@ def load_library():
         lib.gg_grouped_gemm_bf16.restype = ctypes.c_int
         lib.gg_grouped_gemm_bf16_bf16out.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
         lib.gg_grouped_gemm_bf16_bf16out.restype = ctypes.c_int
+        lib.gg_grouped_gemm_bf16_gather.argtypes = [vp, i32, vp, vp, vp, vp, vp, i32, i32, i32, i32,
+                                                    i32, vp]
+        lib.gg_grouped_gemm_bf16_gather.restype = ctypes.c_int
         lib.gg_tile_schedule.argtypes = [vp, i32, i32, i32, i32, vp, vp, i32, vp]
         lib.gg_tile_schedule.restype = ctypes.c_int
         lib.gg_status_string.argtypes = [ctypes.c_int]
@@ -111,6 +114,46 @@ def grouped_gemm(A, B, offsets, out=None, bm: int = 0, stream=None, out_dtype=No
     st = fn(A.data_ptr(), B.data_ptr(), offsets.data_ptr(), out.data_ptr(), E, K, N, M_cap, int(bm),
             _stream_handle(A.device, stream))
     _check(st, fn.__name__)
+    return out
+
+
+def grouped_gemm_gather(X, src_rows, B, offsets, dst_rows=None, out=None, bm: int = 0,
+                        stream=None):
+    """The grouped product with rows gathered and scattered by index, in one launch.
+
+    X: bf16 [n_src, K]; src_rows: int32 [M_cap] (device): grouped row r reads
+    X[src_rows[r]] (rows of expert e are offsets[e]..offsets[e+1]-1);
+    dst_rows: optional int32 [M_cap]: grouped row r is written to
+    out[dst_rows[r]] (default: out[r]); B, offsets, bm, stream as in
+    grouped_gemm; out: optional fp32 [M_cap, N]. Indices out of range read
+    zeros (src) or are not written (dst).
+    """
+    import torch
+    lib = load_library()
+    if X.dtype != torch.bfloat16 or B.dtype != torch.bfloat16:
+        raise TypeError("X and B must be bfloat16")
+    if src_rows.dtype != torch.int32 or offsets.dtype != torch.int32 or (
+            dst_rows is not None and dst_rows.dtype != torch.int32):
+        raise TypeError("src_rows, dst_rows and offsets must be int32")
+    if X.dim() != 2 or B.dim() != 3 or offsets.dim() != 1 or src_rows.dim() != 1:
+        raise ValueError("shapes: X [n_src,K], src_rows [M_cap], B [E,K,N], offsets [E+1]")
+    tensors = [X, B, offsets, src_rows] + ([dst_rows] if dst_rows is not None else [])
+    if not all(t.is_cuda and t.is_contiguous() for t in tensors):
+        raise ValueError("all tensors must be contiguous device tensors")
+    E, K, N = B.shape
+    n_src, M_cap = X.shape[0], src_rows.shape[0]
+    if X.shape[1] != K or offsets.shape[0] != E + 1 or (
+            dst_rows is not None and dst_rows.shape[0] != M_cap):
+        raise ValueError("shape mismatch")
+    if out is None:
+        out = torch.empty((M_cap, N), dtype=torch.float32, device=X.device)
+    elif out.dtype != torch.float32 or tuple(out.shape) != (M_cap, N) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous fp32 [M_cap, N] tensor")
+    st = lib.gg_grouped_gemm_bf16_gather(
+        X.data_ptr(), n_src, src_rows.data_ptr(), B.data_ptr(), offsets.data_ptr(), out.data_ptr(),
+        dst_rows.data_ptr() if dst_rows is not None else None, E, K, N, M_cap, int(bm),
+        _stream_handle(X.device, stream))
+    _check(st, "gg_grouped_gemm_bf16_gather")
     return out
 
 

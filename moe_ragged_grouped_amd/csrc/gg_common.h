@@ -66,6 +66,10 @@ __device__ __forceinline__ u32x4 ld_buf16(buf_rsrc r, uint32_t voff, uint32_t so
   return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
 }
 
+// One 4-byte global load of an index (global_load_dword).
+typedef __attribute__((address_space(1))) const int32_t gbl_ci32;
+__device__ __forceinline__ int ld_g4(const int32_t *p) { return *(gbl_ci32 *)p; }
+
 // One 16-byte global store (global_store_dwordx4).
 __device__ __forceinline__ void st_g16(float *p, f32x4 v) { *(gbl_f32x4 *)p = v; }
 

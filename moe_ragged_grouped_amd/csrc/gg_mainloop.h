@@ -72,13 +72,24 @@ using Cfg64 = TileCfg<64, 64, 1, 8, 1, 2>;    // wave tile 64 x 32
 using Cfg128 = TileCfg<128, 64, 2, 4, 1, 2>;  // wave tile 64 x 64
 using Cfg256 = TileCfg<256, 64, 2, 4, 1, 2>;  // wave tile 128 x 64
 
+// Where a tile's A rows come from and where its C rows go.
+//  Grouped: row r of the tile is row row0 + r of A and of C.
+//  Indexed: row r reads X[src[r]] (src = src_rows + row0) and, when dst is
+//  given, writes C[dst[r]] (dst = dst_rows + row0); otherwise C row row0 + r.
+enum class Rows { Grouped, Indexed };
+
 struct TileArgs {
-  const uint16_t *A;   // A rows of this tile: row r at A + r * K
+  const uint16_t *A;   // Grouped: A rows of this tile (row r at A + r * K); Indexed: X
   const uint16_t *B;   // B[e] + col0: element (k, n) at B + k * N + n
-  void *C;             // C + row0 * N + col0, fp32 or bf16 elements
+  void *C;             // C + row0 * N + col0 (C + col0 when dst is given), fp32 or bf16
   int rows, K, N, ncols;  // ncols = valid columns in this tile (<= BN)
   long long b_bytes;   // bytes from B to the end of B[e]: (K * N - col0) * 2
   int tid;             // threadIdx.x, re-derived per tile (see tile_body)
+  // Indexed rows only
+  const int32_t *src;  // src_rows + row0
+  const int32_t *dst;  // dst_rows + row0, or null
+  int n_src;           // rows of X; a source index outside [0, n_src) reads zeros
+  int n_dst;           // rows of C; a destination outside [0, n_dst) is not written
 };
 
 // Register staging: the A chunks of the next AD K slices (slice s in
@@ -103,17 +114,35 @@ struct Loads {
 
 // Host limits keep every offset below 2^31: rows * K * 2 <= 256 * K * 2 and
 // BK * N * 2 <= 64 * N * 2.
-template <class C>
+template <class C, Rows R>
 __device__ __forceinline__ void init_loads(Loads<C> &L, const TileArgs &t) {
   const int tid = t.tid;
-  L.a = make_buf(t.A, (uint32_t)t.rows * (uint32_t)t.K * 2u);
   const int kc = tid % (C::BK / 8);
   L.a_k = 8 * kc;
+  if constexpr (R == Rows::Grouped) {
+    L.a = make_buf(t.A, (uint32_t)t.rows * (uint32_t)t.K * 2u);
 #pragma unroll
-  for (int i = 0; i < C::A_PER_T; ++i) {
-    const int c = tid + i * kThreads;
-    const uint32_t r = c / (C::BK / 8);
-    L.a_off[i] = c < C::A_CHUNKS ? (r * (uint32_t)t.K + 8u * kc) * 2u : kOob;
+    for (int i = 0; i < C::A_PER_T; ++i) {
+      const int c = tid + i * kThreads;
+      const uint32_t r = c / (C::BK / 8);
+      L.a_off[i] = c < C::A_CHUNKS ? (r * (uint32_t)t.K + 8u * kc) * 2u : kOob;
+    }
+  } else {
+    // the resource spans all of X (n_src * K * 2 <= 2^31 bytes, checked on
+    // the host); a chunk's offset is its source row's, or kOob for padding
+    // rows and for source indices outside [0, n_src)
+    L.a = make_buf(t.A, (uint32_t)t.n_src * (uint32_t)t.K * 2u);
+#pragma unroll
+    for (int i = 0; i < C::A_PER_T; ++i) {
+      const int c = tid + i * kThreads;
+      const int r = c / (C::BK / 8);
+      uint32_t off = kOob;
+      if (c < C::A_CHUNKS && r < t.rows) {
+        const int x = ld_g4(t.src + r);
+        if (x >= 0 && x < t.n_src) off = ((uint32_t)x * (uint32_t)t.K + 8u * kc) * 2u;
+      }
+      L.a_off[i] = off;
+    }
   }
   const int n = 8 * (tid % (C::BN / 8));
 #pragma unroll
@@ -205,8 +234,8 @@ __device__ __forceinline__ void mma_stage(f32x4 (&acc)[C::NI][C::MI], const lds_
 // Full K loop and epilogue for one tile. lds must hold C::LDS_BYTES. Ends with
 // a workgroup barrier, so the next tile may refill the stages at once. O is
 // the element type of C: fp32 (the accumulators as they are) or bf16 (rounded
-// to nearest even in the epilogue).
-template <class C, Out O>
+// to nearest even in the epilogue). R says where rows come from and go.
+template <class C, Out O, Rows R>
 __device__ __forceinline__ void run_tile(const TileArgs &t, lds_u16 *lds) {
   lds_u16 *const As0 = lds;                       // stage s: As0 + s * A_STAGE
   lds_u16 *const Bs0 = lds + C::NS * C::A_STAGE;  // stage s: Bs0 + s * B_STAGE
@@ -232,7 +261,7 @@ __device__ __forceinline__ void run_tile(const TileArgs &t, lds_u16 *lds) {
   // flight.
   const int KT = cdiv(t.K, C::BK);
   Loads<C> L;
-  init_loads<C>(L, t);
+  init_loads<C, R>(L, t);
   Staging<C> st;
   static_for<(C::AD > C::BD ? C::AD : C::BD)>([&](auto jc) {
     constexpr int j = decltype(jc)::value;
@@ -278,15 +307,22 @@ __device__ __forceinline__ void run_tile(const TileArgs &t, lds_u16 *lds) {
 #pragma unroll
   for (int mi = 0; mi < C::MI; ++mi) {
     const int m = wm0 + mi * 16 + s;
-    if (m < t.rows) {
+    int dst_row = m;  // row of t.C this lane writes
+    if constexpr (R == Rows::Indexed) {
+      if (t.dst != nullptr && m < t.rows) {
+        const int d = ld_g4(t.dst + m);
+        dst_row = (d >= 0 && d < t.n_dst) ? d : -1;
+      }
+    }
+    if (m < t.rows && dst_row >= 0) {
 #pragma unroll
       for (int ni = 0; ni < C::NI; ++ni) {
         const int n = wn0 + ni * 16 + 4 * g;
         if (n < t.ncols) {
           if constexpr (O == Out::F32)
-            st_g16((float *)t.C + (size_t)m * t.N + n, acc[ni][mi]);
+            st_g16((float *)t.C + (size_t)dst_row * t.N + n, acc[ni][mi]);
           else
-            st_g8_bf16((uint16_t *)t.C + (size_t)m * t.N + n, acc[ni][mi]);
+            st_g8_bf16((uint16_t *)t.C + (size_t)dst_row * t.N + n, acc[ni][mi]);
         }
       }
     }

@@ -36,6 +36,10 @@ struct Params {
   void *C;  // fp32 or bf16 [M_cap][N]
   int E, K, N, M_cap;
   int bm_fixed;  // 0 = per-expert choice
+  // indexed rows (gather / scatter entry point) only
+  const int32_t *src_rows;  // [M_cap]: grouped row r reads A row src_rows[r]
+  const int32_t *dst_rows;  // [M_cap] or null: grouped row r writes C row dst_rows[r]
+  int n_src;                // rows of A in the indexed form
 };
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
@@ -52,10 +56,12 @@ __device__ __forceinline__ const void *uniform_ptr(const void *p) {
 // to the compiler, so these values live in scalar registers. In the kernel
 // that compiles in all five heights this is what keeps the largest height's
 // path within 256 VGPRs (two waves per SIMD) without spilling.
-template <class Cfg, Out O>
-__device__ __forceinline__ void tile_body(const uint16_t *A, const uint16_t *B, void *C, int K,
-                                          int N, int row0, int rows, int col0, int expert,
-                                          uint32_t lds_addr) {
+template <class Cfg, Out O, Rows R>
+__device__ __forceinline__ void tile_body(const Params &p, int row0, int rows, int col0,
+                                          int expert, uint32_t lds_addr) {
+  const uint16_t *A = p.A, *B = p.B;
+  void *C = p.C;
+  int K = p.K, N = p.N;
   lds_u16 *const lds = (lds_u16 *)(uintptr_t)uniform((int)lds_addr);
   K = uniform(K);
   N = uniform(N);
@@ -63,10 +69,22 @@ __device__ __forceinline__ void tile_body(const uint16_t *A, const uint16_t *B, 
   col0 = uniform(col0);
   expert = uniform(expert);
   TileArgs a;
-  a.A = (const uint16_t *)uniform_ptr(A) + (size_t)row0 * K;
   a.B = (const uint16_t *)uniform_ptr(B) + (size_t)expert * K * N + col0;
   constexpr size_t kOutBytes = O == Out::F32 ? 4 : 2;
-  a.C = (char *)uniform_ptr(C) + ((size_t)row0 * N + col0) * kOutBytes;
+  if constexpr (R == Rows::Grouped) {
+    a.A = (const uint16_t *)uniform_ptr(A) + (size_t)row0 * K;
+    a.C = (char *)uniform_ptr(C) + ((size_t)row0 * N + col0) * kOutBytes;
+    a.src = a.dst = nullptr;
+    a.n_src = a.n_dst = 0;
+  } else {
+    a.A = (const uint16_t *)uniform_ptr(A);
+    a.src = (const int32_t *)uniform_ptr(p.src_rows) + row0;
+    const int32_t *dst = (const int32_t *)uniform_ptr(p.dst_rows);
+    a.dst = dst ? dst + row0 : nullptr;
+    a.C = (char *)uniform_ptr(C) + ((size_t)(dst ? 0 : row0) * N + col0) * kOutBytes;
+    a.n_src = uniform(p.n_src);
+    a.n_dst = uniform(p.M_cap);
+  }
   a.rows = uniform(rows);
   a.K = K;
   a.N = N;
@@ -78,18 +96,18 @@ __device__ __forceinline__ void tile_body(const uint16_t *A, const uint16_t *B, 
   int tid = threadIdx.x;
   asm volatile("" : "+v"(tid));
   a.tid = tid;
-  run_tile<Cfg, O>(a, lds);
+  run_tile<Cfg, O, R>(a, lds);
 }
 
-template <class Cfg, Out O>
+template <class Cfg, Out O, Rows R>
 __device__ __forceinline__ void tile_call(const Params &p, const Tile &t, uint32_t lds_addr) {
-  tile_body<Cfg, O>(p.A, p.B, p.C, p.K, p.N, t.row0, t.rows, t.col0, t.expert, lds_addr);
+  tile_body<Cfg, O, R>(p, t.row0, t.rows, t.col0, t.expert, lds_addr);
 }
 
 // MASK bit c compiles in tile height 16 << c (16, 32, 64, 128, 256). A launch
 // must compile in every height its schedule can produce. O is the element
-// type of C.
-template <int MASK, Out O>
+// type of C; R says whether rows are grouped or gathered/scattered by index.
+template <int MASK, Out O, Rows R>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(Params p) {
   extern __shared__ __attribute__((aligned(16))) uint16_t lds_dyn[];
   __shared__ SchedLds sched;
@@ -106,11 +124,11 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(Params p) {
     if (t >= total) break;
     const Tile tl = decode_tile(sched, p.off, t, p.E, p.M_cap, p.N, p.bm_fixed);
     switch (tl.bm) {
-      case 16: if constexpr (MASK & 1) tile_call<Cfg16, O>(p, tl, lds); break;
-      case 32: if constexpr (MASK & 2) tile_call<Cfg32, O>(p, tl, lds); break;
-      case 64: if constexpr (MASK & 4) tile_call<Cfg64, O>(p, tl, lds); break;
-      case 128: if constexpr (MASK & 8) tile_call<Cfg128, O>(p, tl, lds); break;
-      default: if constexpr (MASK & 16) tile_call<Cfg256, O>(p, tl, lds); break;
+      case 16: if constexpr (MASK & 1) tile_call<Cfg16, O, R>(p, tl, lds); break;
+      case 32: if constexpr (MASK & 2) tile_call<Cfg32, O, R>(p, tl, lds); break;
+      case 64: if constexpr (MASK & 4) tile_call<Cfg64, O, R>(p, tl, lds); break;
+      case 128: if constexpr (MASK & 8) tile_call<Cfg128, O, R>(p, tl, lds); break;
+      default: if constexpr (MASK & 16) tile_call<Cfg256, O, R>(p, tl, lds); break;
     }
   }
 }
@@ -156,7 +174,7 @@ struct LaunchInfo {
 
 constexpr int kMaxDevices = 64;
 
-template <int MASK, Out O>
+template <int MASK, Out O, Rows R>
 static LaunchInfo launch_info(int dev) {
   static LaunchInfo cache[kMaxDevices];
   static std::once_flag once[kMaxDevices];
@@ -166,11 +184,11 @@ static LaunchInfo launch_info(int dev) {
     const int lds = lds_bytes<MASK>();
     li.err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (li.err == hipSuccess)
-      li.err = hipFuncSetAttribute((const void *)grouped_gemm_kernel<MASK, O>,
+      li.err = hipFuncSetAttribute((const void *)grouped_gemm_kernel<MASK, O, R>,
                                    hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (li.err == hipSuccess)
       li.err = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &per_cu, (const void *)grouped_gemm_kernel<MASK, O>, kThreads, lds);
+          &per_cu, (const void *)grouped_gemm_kernel<MASK, O, R>, kThreads, lds);
     if (li.err == hipSuccess) {
       if (per_cu < 1) per_cu = 1;
       li.grid = cus * per_cu;
@@ -182,15 +200,15 @@ static LaunchInfo launch_info(int dev) {
   return cache[dev];
 }
 
-template <int MASK, Out O>
+template <int MASK, Out O, Rows R>
 static gg_status_t launch(const Params &p, long long tile_bound, hipStream_t stream) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return GG_ERR_LAUNCH;
-  const LaunchInfo li = launch_info<MASK, O>(dev);
+  const LaunchInfo li = launch_info<MASK, O, R>(dev);
   if (li.err != hipSuccess) return GG_ERR_LAUNCH;
   long long g = tile_bound < li.grid ? tile_bound : li.grid;
   g = (g + kXcds - 1) / kXcds * kXcds;  // keep a multiple of the XCD count
-  hipLaunchKernelGGL((grouped_gemm_kernel<MASK, O>), dim3((unsigned)g), dim3(kThreads),
+  hipLaunchKernelGGL((grouped_gemm_kernel<MASK, O, R>), dim3((unsigned)g), dim3(kThreads),
                      lds_bytes<MASK>(), stream, p);
   return hipGetLastError() == hipSuccess ? GG_OK : GG_ERR_LAUNCH;
 }
@@ -216,32 +234,42 @@ static gg_status_t check_sizes(const int32_t *off, int E, int N, int M_cap, int 
   return GG_OK;
 }
 
-// The product with C of element type O: argument checks, then one launch.
-template <Out O>
-static gg_status_t grouped_gemm(const void *A, const void *B, const int32_t *group_offsets,
-                                void *C, int32_t E, int32_t K, int32_t N, int32_t M_cap,
-                                int32_t bm, void *stream) {
+// The product with C of element type O and rows of form R: argument checks,
+// then one launch. p arrives with every field but the sizes already set.
+template <Out O, Rows R>
+static gg_status_t grouped_gemm(Params p, void *stream) {
   long long bound = 0;
-  gg_status_t st = check_sizes(group_offsets, E, N, M_cap, bm, &bound);
+  gg_status_t st = check_sizes(p.off, p.E, p.N, p.M_cap, p.bm_fixed, &bound);
   if (st != GG_OK) return st;
-  if (A == nullptr || B == nullptr || C == nullptr || K < 1) return GG_ERR_INVALID_VALUE;
-  if (K % 8 != 0) return GG_ERR_MISALIGNED;
+  if (p.A == nullptr || p.B == nullptr || p.C == nullptr || p.K < 1) return GG_ERR_INVALID_VALUE;
+  if (p.K % 8 != 0) return GG_ERR_MISALIGNED;
   // 32-bit buffer offsets: a tile's A rows (256 * K * 2 bytes) and a K slice
   // of B (64 * N * 2 bytes) must stay below 2^31 bytes
-  if (K > kMaxK || N > kMaxN) return GG_ERR_UNSUPPORTED;
-  if (!aligned(A, 16) || !aligned(B, 16) || !aligned(C, 16)) return GG_ERR_MISALIGNED;
-  if (M_cap == 0 || bound == 0) return GG_OK;
-  Params p{static_cast<const uint16_t *>(A), static_cast<const uint16_t *>(B), group_offsets, C,
-           E, K, N, M_cap, bm};
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  switch (bm) {
-    case 16: return launch<1, O>(p, bound, s);
-    case 32: return launch<2, O>(p, bound, s);
-    case 64: return launch<4, O>(p, bound, s);
-    case 128: return launch<8, O>(p, bound, s);
-    case 256: return launch<16, O>(p, bound, s);
-    default: return launch<31, O>(p, bound, s);
+  if (p.K > kMaxK || p.N > kMaxN) return GG_ERR_UNSUPPORTED;
+  if (!aligned(p.A, 16) || !aligned(p.B, 16) || !aligned(p.C, 16)) return GG_ERR_MISALIGNED;
+  if constexpr (R == Rows::Indexed) {
+    if (p.src_rows == nullptr || p.n_src < 0) return GG_ERR_INVALID_VALUE;
+    if (!aligned(p.src_rows, 4) || (p.dst_rows && !aligned(p.dst_rows, 4)))
+      return GG_ERR_MISALIGNED;
+    // the A resource covers all of X with 32-bit offsets
+    if ((long long)p.n_src * p.K * 2 > (1LL << 31)) return GG_ERR_UNSUPPORTED;
   }
+  if (p.M_cap == 0 || bound == 0) return GG_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  switch (p.bm_fixed) {
+    case 16: return launch<1, O, R>(p, bound, s);
+    case 32: return launch<2, O, R>(p, bound, s);
+    case 64: return launch<4, O, R>(p, bound, s);
+    case 128: return launch<8, O, R>(p, bound, s);
+    case 256: return launch<16, O, R>(p, bound, s);
+    default: return launch<31, O, R>(p, bound, s);
+  }
+}
+
+static Params make_params(const void *A, const void *B, const int32_t *off, void *C, int32_t E,
+                          int32_t K, int32_t N, int32_t M_cap, int32_t bm) {
+  return Params{static_cast<const uint16_t *>(A), static_cast<const uint16_t *>(B), off, C, E, K,
+                N, M_cap, bm, nullptr, nullptr, 0};
 }
 
 }  // namespace gg
@@ -252,14 +280,29 @@ extern "C" gg_status_t gg_grouped_gemm_bf16(const void *A, const void *B,
                                             const int32_t *group_offsets, float *C, int32_t E,
                                             int32_t K, int32_t N, int32_t M_cap, int32_t bm,
                                             void *stream) {
-  return grouped_gemm<Out::F32>(A, B, group_offsets, C, E, K, N, M_cap, bm, stream);
+  return grouped_gemm<Out::F32, Rows::Grouped>(
+      make_params(A, B, group_offsets, C, E, K, N, M_cap, bm), stream);
 }
 
 extern "C" gg_status_t gg_grouped_gemm_bf16_bf16out(const void *A, const void *B,
                                                     const int32_t *group_offsets, void *C,
                                                     int32_t E, int32_t K, int32_t N,
                                                     int32_t M_cap, int32_t bm, void *stream) {
-  return grouped_gemm<Out::BF16>(A, B, group_offsets, C, E, K, N, M_cap, bm, stream);
+  return grouped_gemm<Out::BF16, Rows::Grouped>(
+      make_params(A, B, group_offsets, C, E, K, N, M_cap, bm), stream);
+}
+
+extern "C" gg_status_t gg_grouped_gemm_bf16_gather(const void *X, int32_t n_src,
+                                                   const int32_t *src_rows, const void *B,
+                                                   const int32_t *group_offsets, float *C,
+                                                   const int32_t *dst_rows, int32_t E, int32_t K,
+                                                   int32_t N, int32_t M_cap, int32_t bm,
+                                                   void *stream) {
+  Params p = make_params(X, B, group_offsets, C, E, K, N, M_cap, bm);
+  p.src_rows = src_rows;
+  p.dst_rows = dst_rows;
+  p.n_src = n_src;
+  return grouped_gemm<Out::F32, Rows::Indexed>(p, stream);
 }
 
 extern "C" gg_status_t gg_tile_schedule(const int32_t *group_offsets, int32_t E, int32_t N,

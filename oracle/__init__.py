@@ -29,6 +29,12 @@ Contents
   (A once, B once per expert that has rows, C once).
 * ``adaptive_bm``: the per-expert tile-height rule of the HIP path, written
   from its stated definition (see the function).
+* ``grouped_gemm_indexed``: the same product with A rows gathered from X by a
+  row index list and C rows scattered by a second list -- the definition
+  written out: A = X[src] (zero rows for indices out of range), the grouped
+  product, then C[dst[r]] = C_grouped[r]. The permutation around the GEMM is
+  the worklog's "What I am measuring" scope note; the indexed form is the
+  plain reading of folding it into the loads and stores.
 * ``round_to_bf16``: binary64 -> bfloat16 rounding to nearest, ties to even,
   written from the IEEE-754 definition of the format (8 significant bits,
   fp32's exponent range). It turns the fp64 reference into the bf16 values a
@@ -132,6 +138,35 @@ def grouped_gemm_entries(A, B, offsets, rows, cols):
     if rc != 0:
         raise ValueError("oracle: malformed problem (offsets or sizes)")
     return c, s
+
+
+def grouped_gemm_indexed(X, src_rows, B, offsets, dst_rows=None, M_cap=None):
+    """Gather, grouped product, scatter (all in the plain definition).
+
+    X: bf16 bits [n_src, K]; src_rows: int [M_cap]; B: bf16 bits [E, K, N];
+    offsets: [E+1]; dst_rows: int [M_cap] or None (identity). Returns (C, S)
+    with C, S float64 [M_cap, N]; rows no grouped row writes are NaN.
+    """
+    X = np.asarray(X)
+    src = np.asarray(src_rows, dtype=np.int64)
+    off = np.asarray(offsets, dtype=np.int64)
+    M_cap = len(src) if M_cap is None else int(M_cap)
+    n_src, K = X.shape
+    m_tot = int(off[-1])
+    A = np.zeros((max(m_tot, 1), K), dtype=np.uint16)
+    for r in range(m_tot):
+        if 0 <= src[r] < n_src:
+            A[r] = X[src[r]]
+    Cg, Sg, _ = grouped_gemm(A, B, off, M_cap=max(m_tot, 1))
+    C = np.full((M_cap, B.shape[2]), np.nan)
+    S = np.full((M_cap, B.shape[2]), np.nan)
+    dst = np.arange(M_cap) if dst_rows is None else np.asarray(dst_rows, dtype=np.int64)
+    for r in range(m_tot):
+        d = int(dst[r])
+        if 0 <= d < M_cap:
+            C[d] = Cg[r]
+            S[d] = Sg[r]
+    return C, S
 
 
 def _cdiv(a: int, b: int) -> int:

@@ -86,3 +86,22 @@ def test_tile_schedule_host_checks(lib):
     assert f(64, 4, 256, 29, 7, 128, 128, 10, None) == 1   # bad bm
     assert f(64, 4, 250, 29, 0, 128, 128, 10, None) == 2   # N not multiple of 8
     assert f(0, 4, 256, 29, 0, 128, 128, 10, None) == 1    # offsets NULL
+
+
+def test_gather_host_checks(lib):
+    f = lib.gg_grouped_gemm_bf16_gather
+    #      X   n_src src  B   off  C    dst  E  K    N    M_cap bm
+    ok = [16, 10, 64, 32, 64, 128, 0, 4, 256, 256, 29, 0]
+    def call(**kw):
+        a = list(ok)
+        names = ["X", "n_src", "src", "B", "off", "C", "dst", "E", "K", "N", "M_cap", "bm"]
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return f(*a, None)
+    assert call(src=0) == 1                    # src_rows NULL
+    assert call(n_src=-1) == 1
+    assert call(X=0) == 1
+    assert call(src=66) == 2                   # misaligned index list
+    assert call(dst=70) == 2
+    assert call(n_src=2 ** 22 + 1) == 3        # n_src * K * 2 > 2^31
+    assert call(M_cap=0) == 0                  # nothing to do

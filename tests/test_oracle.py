@@ -317,3 +317,55 @@ def test_round_to_bf16_matches_torch_on_fp32_values():
     # monotone nondecreasing
     xs = np.sort(x)
     assert (np.diff(oracle.round_to_bf16(xs)) >= 0).all()
+
+
+def test_indexed_identity_is_the_grouped_product():
+    w = wl.make_workload(E=3, K=40, N=24, sizes=[5, 0, 9], seed=31)
+    src = np.arange(w.M_cap)
+    c1, s1 = oracle.grouped_gemm_indexed(w.A, src, w.B, w.offsets)
+    c0, s0, _ = oracle.grouped_gemm(w.A, w.B, w.offsets)
+    m = w.M_tot
+    assert np.array_equal(c1[:m], c0[:m]) and np.array_equal(s1[:m], s0[:m])
+    assert np.isnan(c1[m:]).all()
+
+
+def test_indexed_brute_force_gather_scatter():
+    # integer inputs, so every sum is exact; a scalar Python definition of
+    # gather -> per-expert product -> scatter, with an out-of-range source
+    # (zero row) and an out-of-range destination (row not written)
+    rng = np.random.default_rng(32)
+    E, K, N, n_src = 3, 6, 5, 7
+    X = wl.f32_to_bf16_bits(rng.integers(-3, 4, size=(n_src, K)).astype(np.float32))
+    B = wl.f32_to_bf16_bits(rng.integers(-3, 4, size=(E, K, N)).astype(np.float32))
+    off = np.array([0, 3, 3, 8], dtype=np.int32)
+    src = np.array([4, 0, 6, 2, 2, 99, 1, 5, 0, 0])
+    dst = np.array([9, 7, 5, 3, 1, 0, 2, -1, 4, 6])
+    got, _ = oracle.grouped_gemm_indexed(X, src, B, off, dst, M_cap=10)
+    xf, bf = wl.bf16_bits_to_f32(X), wl.bf16_bits_to_f32(B)
+    want = np.full((10, N), np.nan)
+    for e in range(E):
+        for r in range(off[e], off[e + 1]):
+            if not 0 <= dst[r] < 10:
+                continue
+            for j in range(N):
+                acc = 0.0
+                for k in range(K):
+                    a = float(xf[src[r], k]) if 0 <= src[r] < n_src else 0.0
+                    acc += a * float(bf[e, k, j])
+                want[dst[r], j] = acc
+    assert np.array_equal(np.isnan(got), np.isnan(want))
+    assert np.array_equal(got[~np.isnan(got)], want[~np.isnan(want)])
+    assert (got[0] == 0).all()  # grouped row 5 reads source 99 -> zero row
+
+
+def test_indexed_permutation_invariance():
+    # permuting the source rows and the index list together changes nothing
+    w = wl.make_workload(E=4, K=48, N=32, sizes=[7, 3, 0, 11], seed=33)
+    rng = np.random.default_rng(34)
+    perm = rng.permutation(w.M_cap)
+    X = w.A[perm]
+    inv = np.argsort(perm)
+    c1, _ = oracle.grouped_gemm_indexed(X, inv, w.B, w.offsets)
+    c0, _, _ = oracle.grouped_gemm(w.A, w.B, w.offsets)
+    m = w.M_tot
+    assert np.array_equal(c1[:m], c0[:m])

@@ -347,3 +347,134 @@ def test_bf16_out_full_size_sampled(gg):
     rows, cols = _samples(w, rng)
     c, s = oracle.grouped_gemm_entries(w.A, w.B, w.offsets, rows, cols)
     parity.check_bf16(out[rows, cols], c, s, "uniform16k bf16 sampled")
+
+
+# ---- rows gathered / scattered by index -------------------------------------------
+
+def _topk_routing(n_tokens, E, topk, rng):
+    """Top-k routing of n_tokens onto E experts, as index lists: grouped row r
+    (rows sorted by expert) reads token src[r] and lands in output row
+    dst[r] = token * topk + slot (token-major, one row per routed pair)."""
+    pairs = []
+    for t in range(n_tokens):
+        for slot, e in enumerate(rng.choice(E, size=topk, replace=False)):
+            pairs.append((int(e), t, slot))
+    pairs.sort()
+    sizes = np.bincount([p[0] for p in pairs], minlength=E)
+    src = np.array([p[1] for p in pairs], dtype=np.int32)
+    dst = np.array([p[1] * topk + p[2] for p in pairs], dtype=np.int32)
+    return sizes, src, dst
+
+
+def _gather_case(gg, n_tokens, E, K, N, topk, seed, bm, use_dst=True, pad=0):
+    rng = np.random.default_rng(seed)
+    sizes, src, dst = _topk_routing(n_tokens, E, topk, rng)
+    w = wl.make_workload(E=E, K=K, N=N, sizes=[int(x) for x in sizes], seed=seed,
+                         M_cap=int(sizes.sum()) + pad)
+    X = wl.make_workload(E=1, K=K, N=8, sizes=[n_tokens], seed=seed + 1000).A  # token rows
+    M_cap = w.M_cap
+    src_full = np.concatenate([src, np.full(pad, -1, np.int32)])
+    dst_full = np.concatenate([dst, np.full(pad, -1, np.int32)])
+    dev = torch.device("cuda:0")
+    Xd = torch.from_numpy(X.view(np.int16)).to(dev).view(torch.bfloat16)
+    Bd = torch.from_numpy(w.B.view(np.int16)).to(dev).view(torch.bfloat16)
+    off = torch.from_numpy(w.offsets).to(dev)
+    sd = torch.from_numpy(src_full).to(dev)
+    dd = torch.from_numpy(dst_full).to(dev) if use_dst else None
+    C = torch.full((M_cap, N), float("nan"), dtype=torch.float32, device=dev)
+    _say("case gather tokens=%d E=%d K=%d N=%d topk=%d bm=%d dst=%s" % (n_tokens, E, K, N, topk, bm, use_dst))
+    gg.grouped_gemm_gather(Xd, sd, Bd, off, dst_rows=dd, out=C, bm=bm)
+    torch.cuda.synchronize()
+    got = C.cpu().numpy()
+    ref, s = oracle.grouped_gemm_indexed(X, src_full, w.B, w.offsets, dst_full if use_dst else None,
+                                         M_cap=M_cap)
+    written = ~np.isnan(ref[:, 0])
+    assert np.array_equal(np.isnan(got[:, 0]), ~written), "written rows differ"
+    parity.check(got[written], ref[written], s[written], "gather")
+    return got, w, X, src_full
+
+
+@pytest.mark.parametrize("bm", BMS)
+def test_gather_scatter_topk(gg, bm):
+    _gather_case(gg, n_tokens=150, E=8, K=200, N=520, topk=2, seed=41, bm=bm)
+
+
+@pytest.mark.parametrize("bm", [0, 128])
+def test_gather_grouped_output(gg, bm):
+    _gather_case(gg, n_tokens=97, E=5, K=136, N=264, topk=3, seed=42, bm=bm, use_dst=False)
+
+
+def test_gather_out_of_range_indices(gg):
+    # source indices outside [0, n_src) read zeros; destinations outside
+    # [0, M_cap) are not written; rows past off[E] are never touched
+    rng = np.random.default_rng(43)
+    E, K, N, n_src = 3, 72, 264, 40
+    sizes = [10, 0, 20]
+    w = wl.make_workload(E=E, K=K, N=N, sizes=sizes, seed=43, M_cap=36)
+    X = wl.make_workload(E=1, K=K, N=8, sizes=[n_src], seed=44).A
+    src = rng.integers(0, n_src, size=36).astype(np.int32)
+    src[[0, 7, 15]] = [n_src, -3, 2 ** 30]
+    dst = rng.permutation(36).astype(np.int32)
+    dst[[3, 20]] = [36, -1]
+    dev = torch.device("cuda:0")
+    C = torch.full((36, N), float("nan"), dtype=torch.float32, device=dev)
+    _say("case gather out-of-range")
+    gg.grouped_gemm_gather(torch.from_numpy(X.view(np.int16)).to(dev).view(torch.bfloat16),
+                           torch.from_numpy(src).to(dev),
+                           torch.from_numpy(w.B.view(np.int16)).to(dev).view(torch.bfloat16),
+                           torch.from_numpy(w.offsets).to(dev), dst_rows=torch.from_numpy(dst).to(dev),
+                           out=C, bm=0)
+    torch.cuda.synchronize()
+    got = C.cpu().numpy()
+    ref, s = oracle.grouped_gemm_indexed(X, src, w.B, w.offsets, dst, M_cap=36)
+    written = ~np.isnan(ref[:, 0])
+    assert np.array_equal(np.isnan(got[:, 0]), ~written)
+    parity.check(got[written], ref[written], s[written], "gather out-of-range")
+    assert (got[dst[0]] == 0).all()  # grouped row 0 read an out-of-range source
+
+
+def test_gather_equals_pregathered_grouped(gg):
+    # same products in the same K order as the grouped entry point on X[src]
+    got, w, X, src = _gather_case(gg, n_tokens=120, E=6, K=328, N=392, topk=2, seed=45, bm=0,
+                                  use_dst=False)
+    dev = torch.device("cuda:0")
+    A = X[src]
+    Ad = torch.from_numpy(np.ascontiguousarray(A).view(np.int16)).to(dev).view(torch.bfloat16)
+    Bd = torch.from_numpy(w.B.view(np.int16)).to(dev).view(torch.bfloat16)
+    c = gg.grouped_gemm(Ad, Bd, torch.from_numpy(w.offsets).to(dev), bm=0)
+    torch.cuda.synchronize()
+    m = w.M_tot
+    assert np.array_equal(got[:m], c.cpu().numpy()[:m])
+
+
+def test_gather_decode_shape_sampled(gg):
+    # the decode shape reached through routing: 64 tokens, top-8, 32 experts,
+    # 16 rows each, K=6144, N=4096, output token-major
+    E, K, N, topk, n_tokens = 32, 6144, 4096, 8, 64
+    pairs = sorted(((t * topk + j) % E, t, j) for t in range(n_tokens) for j in range(topk))
+    sizes = np.bincount([p[0] for p in pairs], minlength=E)
+    assert (sizes == 16).all()
+    src = np.array([p[1] for p in pairs], dtype=np.int32)
+    dst = np.array([p[1] * topk + p[2] for p in pairs], dtype=np.int32)
+    w = _full("decode")
+    X = wl.make_workload(E=1, K=K, N=8, sizes=[n_tokens], seed=46).A
+    dev = torch.device("cuda:0")
+    C = torch.full((512, N), float("nan"), dtype=torch.float32, device=dev)
+    _say("case gather decode shape")
+    gg.grouped_gemm_gather(torch.from_numpy(X.view(np.int16)).to(dev).view(torch.bfloat16),
+                           torch.from_numpy(src).to(dev),
+                           torch.from_numpy(w.B.view(np.int16)).to(dev).view(torch.bfloat16),
+                           torch.from_numpy(w.offsets).to(dev), dst_rows=torch.from_numpy(dst).to(dev),
+                           out=C, bm=0)
+    torch.cuda.synchronize()
+    out = C.cpu().numpy()
+    assert np.isfinite(out).all()
+    # sampled entries: output row token*topk + slot = grouped row r
+    rng = np.random.default_rng(9)
+    r = rng.integers(0, 512, size=2000)
+    cols = rng.integers(0, N, size=2000)
+    A = X[src]
+    c, s = oracle.grouped_gemm_entries(np.ascontiguousarray(A), w.B, w.offsets, r, cols)
+    got = out[dst[r], cols]
+    d = np.abs(got - c)
+    assert (d <= parity.ELEM * s).all()

@@ -62,13 +62,14 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(config, bm, out="fp32"):
+def measured_traffic(config, bm, out="fp32", weights="bf16"):
     """HBM bytes per launch from the committed counter summary, if still current."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     try:
-        key = "%s/bm%d" % (config, bm) + ("" if out == "fp32" else "/" + out)
+        key = ("%s/bm%d" % (config, bm) + ("" if out == "fp32" else "/" + out)
+               + ("" if weights == "bf16" else "/%sw" % weights))
         rec = json.load(open(path)).get(key)
     except (OSError, ValueError):
         return None
@@ -121,6 +122,8 @@ def main():
                          "the GPU clocks have left their idle state when timing starts")
     ap.add_argument("--out", default="fp32", choices=("fp32", "bf16"),
                     help="element type of C (bf16: rounded in the epilogue)")
+    ap.add_argument("--weights", default="bf16", choices=("bf16", "fp8"),
+                    help="fp8: E4M3 weights with per-column scales (a separate precision)")
     ap.add_argument("--gather", action="store_true",
                     help="time the gather/scatter entry point (A rows and C rows by index)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -161,6 +164,15 @@ def main():
     off = torch.from_numpy(w.offsets).to(dev)
     c_dtype = torch.float32 if args.out == "fp32" else torch.bfloat16
     C = torch.empty((w.M_cap, w.N), dtype=c_dtype, device=dev)
+    if args.weights == "fp8":
+        # fp8 E4M3 weights with per-(expert, column) fp32 scales, quantized
+        # from the bf16 weights on the host (input recipe, untimed)
+        if args.out != "fp32" or args.gather:
+            raise SystemExit("--weights fp8 times the fp32-output grouped-row entry point")
+        q_np, sc_np = wl.fp8_weights(w)
+        Bq = torch.from_numpy(q_np).to(dev)
+        Bs = torch.from_numpy(sc_np).to(dev)
+        del q_np
     if args.gather:
         # rows reached by index: X holds the routed rows in a seeded random
         # (token) order, grouped row r reads X[perm[r]] and is written back to
@@ -173,7 +185,9 @@ def main():
         perm = torch.from_numpy(perm_np).to(dev)
 
     def step():
-        if args.gather:
+        if args.weights == "fp8":
+            gg.grouped_gemm_fp8w(A, Bq, Bs, off, out=C, bm=args.bm)
+        elif args.gather:
             gg.grouped_gemm_gather(X, perm, B, off, dst_rows=perm, out=C, bm=args.bm)
         else:
             gg.grouped_gemm(A, B, off, out=C, bm=args.bm)
@@ -214,12 +228,14 @@ def main():
 
     useful = 2.0 * w.M_tot * w.K * w.N
     c_bytes = 4 if args.out == "fp32" else 2
-    alg_bytes = (2 * w.M_tot * w.K + 2 * w.K * w.N * int((w.sizes > 0).sum())
-                 + c_bytes * w.M_tot * w.N + (8 * w.M_tot if args.gather else 0))
+    active = int((w.sizes > 0).sum())
+    b_bytes = 2 * w.K * w.N * active if args.weights == "bf16" else (w.K + 4) * w.N * active
+    alg_bytes = (2 * w.M_tot * w.K + b_bytes + c_bytes * w.M_tot * w.N
+                 + (8 * w.M_tot if args.gather else 0))
     intensity = useful / alg_bytes
     hbm_gbs = alg_bytes / launch_s / 1e9
     tflops_launch = useful / launch_s / 1e12
-    traffic = None if args.gather else measured_traffic(args.config, args.bm, args.out)
+    traffic = None if args.gather else measured_traffic(args.config, args.bm, args.out, args.weights)
     if intensity < RIDGE:
         roof = {"bound": "hbm", "achieved": round(hbm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(hbm_gbs / HBM_PEAK_GBS, 4), "traffic": traffic}
@@ -248,11 +264,13 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16" if args.weights == "bf16" else "fp8w-bf16",
         "data": "synthetic (seeded normal draws rounded to bf16, no dataset)",
         "config": {"workload": DESCRIPTIONS[args.config], "name": args.config, "E": w.E, "K": w.K,
                    "N": w.N, "M_tot": w.M_tot, "bm": args.bm or "per-expert", "out_dtype": args.out,
-                   "rows": "gathered/scattered by index" if args.gather else "grouped"},
+                   "rows": "gathered/scattered by index" if args.gather else "grouped",
+                   "weights": "bf16" if args.weights == "bf16"
+                   else "fp8 e4m3 + fp32 scale per expert column"},
         "hbm_gbs": round(hbm_gbs, 1),
         "hbm_frac": round(hbm_gbs / HBM_PEAK_GBS, 4),
         "mfma_frac": round(tflops_launch / MFMA_BF16_PEAK_TFLOPS, 4),

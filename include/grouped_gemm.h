@@ -131,6 +131,31 @@ gg_status_t gg_grouped_gemm_bf16_gather(const void *X, int32_t n_src, const int3
                                         int32_t M_cap, int32_t bm, void *stream);
 
 /*
+ * gg_grouped_gemm_fp8w -- the product with fp8 weights and per-column scales
+ * (the Pearl Pulse article, "What the 15% measures", notes that its kernel
+ * ships with an FP8 scheme; the scheme below is this library's reading).
+ *
+ *   C[r][n] = scale[e][n] * sum_k A[r][k] * dec(Bq[e][k][n])   for r in group e
+ *
+ *   A        bf16 [M_cap][K], as in gg_grouped_gemm_bf16.
+ *   Bq       uint8 [E][K][N], row-major, 16-byte aligned: OCP fp8 E4M3 codes
+ *            (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; 0x7F and
+ *            0xFF are NaN; largest finite magnitude 448).
+ *   b_scale  fp32 [E][N] on the device, 16-byte aligned: one scale per expert
+ *            and output column.
+ *   C        fp32 [M_cap][N].
+ * Each fp8 weight is widened exactly to bf16 on its way into LDS, the products
+ * accumulate in fp32 in the bf16 matrix cores, and the epilogue multiplies by
+ * the column scale (one more fp32 rounding). Weight bytes in HBM are halved;
+ * this is a separate precision from gg_grouped_gemm_bf16, not a replacement.
+ * Other arguments and rules are those of gg_grouped_gemm_bf16; b_scale NULL
+ * is GG_ERR_INVALID_VALUE, misaligned b_scale GG_ERR_MISALIGNED.
+ */
+gg_status_t gg_grouped_gemm_fp8w(const void *A, const void *Bq, const float *b_scale,
+                                 const int32_t *group_offsets, float *C, int32_t E, int32_t K,
+                                 int32_t N, int32_t M_cap, int32_t bm, void *stream);
+
+/*
  * gg_tile_schedule -- the flat tile list the product kernel consumes,
  * written out (worklog section 2: one descriptor per output tile of one
  * expert, expert-major order, tiles stopping at expert boundaries, empty

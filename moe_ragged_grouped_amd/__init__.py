@@ -14,7 +14,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["grouped_gemm", "grouped_gemm_gather", "tile_schedule", "library_path", "load_library", "GroupedGemmError",
+__all__ = ["grouped_gemm", "grouped_gemm_gather", "grouped_gemm_fp8w", "tile_schedule", "library_path", "load_library", "GroupedGemmError",
            "BM_CHOICES", "TILE_N", "TILE_WIDTH", "MAX_EXPERTS", "SYMBOLS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -25,7 +25,7 @@ TILE_N = 256                      # tile width (every height)
 TILE_WIDTH = {h: TILE_N for h in BM_CHOICES}  # per tile height
 MAX_EXPERTS = 1024
 SYMBOLS = ("gg_grouped_gemm_bf16", "gg_grouped_gemm_bf16_bf16out", "gg_grouped_gemm_bf16_gather",
-           "gg_tile_schedule", "gg_status_string")
+           "gg_grouped_gemm_fp8w", "gg_tile_schedule", "gg_status_string")
 
 _lib = None
 
@@ -54,6 +54,8 @@ def load_library():
         lib.gg_grouped_gemm_bf16_gather.argtypes = [vp, i32, vp, vp, vp, vp, vp, i32, i32, i32, i32,
                                                     i32, vp]
         lib.gg_grouped_gemm_bf16_gather.restype = ctypes.c_int
+        lib.gg_grouped_gemm_fp8w.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
+        lib.gg_grouped_gemm_fp8w.restype = ctypes.c_int
         lib.gg_tile_schedule.argtypes = [vp, i32, i32, i32, i32, vp, vp, i32, vp]
         lib.gg_tile_schedule.restype = ctypes.c_int
         lib.gg_status_string.argtypes = [ctypes.c_int]
@@ -154,6 +156,38 @@ def grouped_gemm_gather(X, src_rows, B, offsets, dst_rows=None, out=None, bm: in
         dst_rows.data_ptr() if dst_rows is not None else None, E, K, N, M_cap, int(bm),
         _stream_handle(X.device, stream))
     _check(st, "gg_grouped_gemm_bf16_gather")
+    return out
+
+
+def grouped_gemm_fp8w(A, Bq, b_scale, offsets, out=None, bm: int = 0, stream=None):
+    """The grouped product with fp8 (OCP E4M3) weights and per-column scales.
+
+    A: bf16 [M_cap, K]; Bq: uint8 (or float8_e4m3fn) [E, K, N]; b_scale: fp32
+    [E, N]; offsets: int32 [E+1]. out[r, n] = b_scale[e, n] * sum_k A[r, k] *
+    Bq[e, k, n] for the rows r of expert e (fp32 [M_cap, N]).
+    """
+    import torch
+    lib = load_library()
+    if A.dtype != torch.bfloat16 or Bq.dtype not in (torch.uint8, torch.float8_e4m3fn):
+        raise TypeError("A must be bfloat16 and Bq uint8 / float8_e4m3fn")
+    if b_scale.dtype != torch.float32 or offsets.dtype != torch.int32:
+        raise TypeError("b_scale must be float32 and offsets int32")
+    if A.dim() != 2 or Bq.dim() != 3 or b_scale.dim() != 2 or offsets.dim() != 1:
+        raise ValueError("shapes: A [M_cap,K], Bq [E,K,N], b_scale [E,N], offsets [E+1]")
+    if not all(t.is_cuda and t.is_contiguous() for t in (A, Bq, b_scale, offsets)):
+        raise ValueError("all tensors must be contiguous device tensors")
+    E, K, N = Bq.shape
+    M_cap = A.shape[0]
+    if A.shape[1] != K or tuple(b_scale.shape) != (E, N) or offsets.shape[0] != E + 1:
+        raise ValueError("shape mismatch")
+    if out is None:
+        out = torch.empty((M_cap, N), dtype=torch.float32, device=A.device)
+    elif out.dtype != torch.float32 or tuple(out.shape) != (M_cap, N) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous fp32 [M_cap, N] tensor")
+    st = lib.gg_grouped_gemm_fp8w(A.data_ptr(), Bq.data_ptr(), b_scale.data_ptr(), offsets.data_ptr(),
+                                  out.data_ptr(), E, K, N, M_cap, int(bm),
+                                  _stream_handle(A.device, stream))
+    _check(st, "gg_grouped_gemm_fp8w")
     return out
 
 

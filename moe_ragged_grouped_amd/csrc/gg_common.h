@@ -70,6 +70,26 @@ __device__ __forceinline__ u32x4 ld_buf16(buf_rsrc r, uint32_t voff, uint32_t so
 typedef __attribute__((address_space(1))) const int32_t gbl_ci32;
 __device__ __forceinline__ int ld_g4(const int32_t *p) { return *(gbl_ci32 *)p; }
 
+// One 16-byte global load of four floats (global_load_dwordx4).
+typedef __attribute__((address_space(1))) const f32x4 gbl_cf32x4;
+__device__ __forceinline__ f32x4 ld_g16f(const float *p) { return *(gbl_cf32x4 *)p; }
+
+// 16 fp8 e4m3 values (OCP, as v_cvt_scalef32_pk_bf16_fp8 reads them) ->
+// 16 bf16 values, in order: lo holds elements 0..7, hi 8..15. Each
+// instruction converts the two fp8 bytes of one 16-bit half of a dword; the
+// scale operand is 1, so the conversion is exact.
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+template <bool HIGH>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HIGH));
+}
+__device__ __forceinline__ void fp8x16_to_bf16x16(u32x4 in, u32x4 &lo, u32x4 &hi) {
+  lo = u32x4{fp8x2_to_bf16x2<false>(in.x), fp8x2_to_bf16x2<true>(in.x),
+             fp8x2_to_bf16x2<false>(in.y), fp8x2_to_bf16x2<true>(in.y)};
+  hi = u32x4{fp8x2_to_bf16x2<false>(in.z), fp8x2_to_bf16x2<true>(in.z),
+             fp8x2_to_bf16x2<false>(in.w), fp8x2_to_bf16x2<true>(in.w)};
+}
+
 // One 16-byte global store (global_store_dwordx4).
 __device__ __forceinline__ void st_g16(float *p, f32x4 v) { *(gbl_f32x4 *)p = v; }
 

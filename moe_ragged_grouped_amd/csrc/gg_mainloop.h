@@ -38,7 +38,7 @@
 
 namespace gg {
 
-template <int BM_, int BK_, int WM_, int WN_, int AD_, int BD_, int NS_ = 2>
+template <int BM_, int BK_, int WM_, int WN_, int AD_, int BD_, bool FP8B_ = false, int NS_ = 2>
 struct TileCfg {
   static constexpr int BM = BM_, BN = width_of(BM_), BK = BK_, WM = WM_, WN = WN_;
   // K slices of A and of B held in registers ahead of the LDS stage
@@ -47,6 +47,11 @@ struct TileCfg {
   // (one barrier per slice); 1 = write after a second barrier (half the LDS)
   static constexpr int NS = NS_;
   static_assert(NS == 1 || NS == 2, "LDS stages");
+  // B in HBM: bf16 (2 bytes) or fp8 e4m3 (1 byte, widened to bf16 on its way
+  // into LDS); one 16-byte global chunk holds B_CE elements of a B row
+  static constexpr bool FP8B = FP8B_;
+  static constexpr int B_ELEM = FP8B ? 1 : 2;
+  static constexpr int B_CE = 16 / B_ELEM;
   static_assert(WM * WN == kThreads / kWave, "one wave per wave tile");
   static_assert(AD >= 1 && AD <= 3 && BD >= 1 && BD <= 4, "prefetch depths");
   static constexpr int WTM = BM / WM;  // rows of C per wave
@@ -59,7 +64,7 @@ struct TileCfg {
   static constexpr int A_STAGE = BM * A_LD;
   static constexpr int B_STAGE = BK * B_LD;
   static constexpr int A_CHUNKS = BM * BK / 8;  // 16-byte chunks per K slice
-  static constexpr int B_CHUNKS = BK * BN / 8;
+  static constexpr int B_CHUNKS = BK * BN / B_CE;
   static constexpr int A_PER_T = (A_CHUNKS + kThreads - 1) / kThreads;
   static constexpr int B_PER_T = (B_CHUNKS + kThreads - 1) / kThreads;
   static constexpr int LDS_BYTES = NS * (A_STAGE + B_STAGE) * 2;
@@ -72,6 +77,15 @@ using Cfg64 = TileCfg<64, 64, 1, 8, 1, 2>;    // wave tile 64 x 32
 using Cfg128 = TileCfg<128, 64, 2, 4, 1, 2>;  // wave tile 64 x 64
 using Cfg256 = TileCfg<256, 64, 2, 4, 1, 2>;  // wave tile 128 x 64
 
+// The same shapes with fp8 weights. A 64-deep fp8 slice of B is half the
+// bytes of a bf16 one; the weight-streaming heights take 128-deep slices so
+// that each CU keeps as many weight bytes in flight as with bf16.
+using Cfg16F = TileCfg<16, 128, 1, 8, 1, 2, true>;
+using Cfg32F = TileCfg<32, 128, 1, 8, 1, 2, true>;
+using Cfg64F = TileCfg<64, 64, 1, 8, 1, 2, true>;
+using Cfg128F = TileCfg<128, 64, 2, 4, 1, 2, true>;
+using Cfg256F = TileCfg<256, 64, 2, 4, 1, 2, true>;
+
 // Where a tile's A rows come from and where its C rows go.
 //  Grouped: row r of the tile is row row0 + r of A and of C.
 //  Indexed: row r reads X[src[r]] (src = src_rows + row0) and, when dst is
@@ -80,10 +94,11 @@ enum class Rows { Grouped, Indexed };
 
 struct TileArgs {
   const uint16_t *A;   // Grouped: A rows of this tile (row r at A + r * K); Indexed: X
-  const uint16_t *B;   // B[e] + col0: element (k, n) at B + k * N + n
+  const char *B;       // B[e] + col0: element (k, n) at byte (k * N + n) * B_ELEM
   void *C;             // C + row0 * N + col0 (C + col0 when dst is given), fp32 or bf16
   int rows, K, N, ncols;  // ncols = valid columns in this tile (<= BN)
-  long long b_bytes;   // bytes from B to the end of B[e]: (K * N - col0) * 2
+  long long b_bytes;   // bytes from B to the end of B[e]: (K * N - col0) * B_ELEM
+  const float *scale;  // fp8 B: scale[e][col0 ..], one per output column; else null
   int tid;             // threadIdx.x, re-derived per tile (see tile_body)
   // Indexed rows only
   const int32_t *src;  // src_rows + row0
@@ -105,7 +120,7 @@ struct Staging {
 // steps by the thread count, a multiple of the chunks per row.
 template <class C>
 struct Loads {
-  static_assert(kThreads % (C::BK / 8) == 0 && kThreads % (C::BN / 8) == 0, "chunk layout");
+  static_assert(kThreads % (C::BK / 8) == 0 && kThreads % (C::BN / C::B_CE) == 0, "chunk layout");
   buf_rsrc a;                   // the tile's valid A rows: rows * K * 2 bytes
   uint32_t a_off[C::A_PER_T];   // chunk i of this thread at k0 = 0, or kOob
   uint32_t b_off[C::B_PER_T];   // chunk i of this thread inside a slice, or kOob
@@ -144,12 +159,12 @@ __device__ __forceinline__ void init_loads(Loads<C> &L, const TileArgs &t) {
       L.a_off[i] = off;
     }
   }
-  const int n = 8 * (tid % (C::BN / 8));
+  const int n = C::B_CE * (tid % (C::BN / C::B_CE));
 #pragma unroll
   for (int i = 0; i < C::B_PER_T; ++i) {
     const int c = tid + i * kThreads;
-    const uint32_t kr = c / (C::BN / 8);
-    L.b_off[i] = (c < C::B_CHUNKS && n < t.ncols) ? (kr * (uint32_t)t.N + n) * 2u : kOob;
+    const uint32_t kr = c / (C::BN / C::B_CE);
+    L.b_off[i] = (c < C::B_CHUNKS && n < t.ncols) ? (kr * (uint32_t)t.N + n) * C::B_ELEM : kOob;
   }
 }
 
@@ -169,9 +184,9 @@ template <class C>
 __device__ __forceinline__ void load_b(u32x4 (&b)[C::B_PER_T], const Loads<C> &L,
                                        const TileArgs &t, int k0) {
   // bytes from the slice start to the end of B[e]; none for a slice past K
-  const long long rem = t.b_bytes - (long long)k0 * t.N * 2;
+  const long long rem = t.b_bytes - (long long)k0 * t.N * C::B_ELEM;
   const uint32_t size = rem <= 0 ? 0u : (rem < kOob ? (uint32_t)rem : kOob);
-  const buf_rsrc r = make_buf(t.B + (size_t)k0 * t.N, size);
+  const buf_rsrc r = make_buf(t.B + (size_t)k0 * t.N * C::B_ELEM, size);
 #pragma unroll
   for (int i = 0; i < C::B_PER_T; ++i) b[i] = ld_buf16(r, L.b_off[i], 0u);
 }
@@ -193,9 +208,19 @@ __device__ __forceinline__ void store_b(const u32x4 (&b)[C::B_PER_T], lds_u16 *B
 #pragma unroll
   for (int i = 0; i < C::B_PER_T; ++i) {
     const int c = tid + i * kThreads;
-    const int kr = c / (C::BN / 8), nc = c % (C::BN / 8);
-    if (C::B_CHUNKS % kThreads == 0 || c < C::B_CHUNKS)
-      *(lds_u32x4 *)(Bs + kr * C::B_LD + 8 * nc) = b[i];
+    const int kr = c / (C::BN / C::B_CE), nc = c % (C::BN / C::B_CE);
+    if (C::B_CHUNKS % kThreads == 0 || c < C::B_CHUNKS) {
+      lds_u16 *dst = Bs + kr * C::B_LD + C::B_CE * nc;
+      if constexpr (C::FP8B) {
+        // 16 fp8 values -> 16 bf16 (exact: every e4m3 value is a bf16 value)
+        u32x4 lo, hi;
+        fp8x16_to_bf16x16(b[i], lo, hi);
+        *(lds_u32x4 *)dst = lo;
+        *(lds_u32x4 *)(dst + 8) = hi;
+      } else {
+        *(lds_u32x4 *)dst = b[i];
+      }
+    }
   }
 }
 
@@ -319,10 +344,12 @@ __device__ __forceinline__ void run_tile(const TileArgs &t, lds_u16 *lds) {
       for (int ni = 0; ni < C::NI; ++ni) {
         const int n = wn0 + ni * 16 + 4 * g;
         if (n < t.ncols) {
+          f32x4 v = acc[ni][mi];
+          if constexpr (C::FP8B) v *= ld_g16f(t.scale + n);  // per-column weight scale
           if constexpr (O == Out::F32)
-            st_g16((float *)t.C + (size_t)dst_row * t.N + n, acc[ni][mi]);
+            st_g16((float *)t.C + (size_t)dst_row * t.N + n, v);
           else
-            st_g8_bf16((uint16_t *)t.C + (size_t)dst_row * t.N + n, acc[ni][mi]);
+            st_g8_bf16((uint16_t *)t.C + (size_t)dst_row * t.N + n, v);
         }
       }
     }

@@ -22,10 +22,14 @@
 #include "gg_schedule.h"
 
 #include <mutex>
+#include <type_traits>
 
 namespace gg {
 
 constexpr int kXcds = 8;
+
+template <bool F8, class Bf16Cfg, class Fp8Cfg>
+using Pick = typename std::conditional<F8, Fp8Cfg, Bf16Cfg>::type;
 constexpr int kMaxK = 1 << 22;
 constexpr int kMaxN = 1 << 24;
 
@@ -40,6 +44,7 @@ struct Params {
   const int32_t *src_rows;  // [M_cap]: grouped row r reads A row src_rows[r]
   const int32_t *dst_rows;  // [M_cap] or null: grouped row r writes C row dst_rows[r]
   int n_src;                // rows of A in the indexed form
+  const float *b_scale;     // fp8 weights only: [E][N] per-column scales
 };
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
@@ -69,7 +74,9 @@ __device__ __forceinline__ void tile_body(const Params &p, int row0, int rows, i
   col0 = uniform(col0);
   expert = uniform(expert);
   TileArgs a;
-  a.B = (const uint16_t *)uniform_ptr(B) + (size_t)expert * K * N + col0;
+  a.B = (const char *)uniform_ptr(B) + ((size_t)expert * K * N + col0) * Cfg::B_ELEM;
+  a.scale = Cfg::FP8B ? (const float *)uniform_ptr(p.b_scale) + (size_t)expert * N + col0
+                      : nullptr;
   constexpr size_t kOutBytes = O == Out::F32 ? 4 : 2;
   if constexpr (R == Rows::Grouped) {
     a.A = (const uint16_t *)uniform_ptr(A) + (size_t)row0 * K;
@@ -89,7 +96,7 @@ __device__ __forceinline__ void tile_body(const Params &p, int row0, int rows, i
   a.K = K;
   a.N = N;
   a.ncols = min(Cfg::BN, N - col0);
-  a.b_bytes = ((long long)K * N - col0) * 2;
+  a.b_bytes = ((long long)K * N - col0) * Cfg::B_ELEM;
   // The per-thread index arithmetic of a tile depends only on threadIdx.x; an
   // opaque copy per tile keeps the compiler from hoisting all of it out of
   // the persistent loop, where it would stay live (and spill) across tiles.
@@ -106,8 +113,9 @@ __device__ __forceinline__ void tile_call(const Params &p, const Tile &t, uint32
 
 // MASK bit c compiles in tile height 16 << c (16, 32, 64, 128, 256). A launch
 // must compile in every height its schedule can produce. O is the element
-// type of C; R says whether rows are grouped or gathered/scattered by index.
-template <int MASK, Out O, Rows R>
+// type of C; R says whether rows are grouped or gathered/scattered by index;
+// F8 selects fp8 weights with per-column scales.
+template <int MASK, Out O, Rows R, bool F8>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(Params p) {
   extern __shared__ __attribute__((aligned(16))) uint16_t lds_dyn[];
   __shared__ SchedLds sched;
@@ -124,11 +132,15 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(Params p) {
     if (t >= total) break;
     const Tile tl = decode_tile(sched, p.off, t, p.E, p.M_cap, p.N, p.bm_fixed);
     switch (tl.bm) {
-      case 16: if constexpr (MASK & 1) tile_call<Cfg16, O, R>(p, tl, lds); break;
-      case 32: if constexpr (MASK & 2) tile_call<Cfg32, O, R>(p, tl, lds); break;
-      case 64: if constexpr (MASK & 4) tile_call<Cfg64, O, R>(p, tl, lds); break;
-      case 128: if constexpr (MASK & 8) tile_call<Cfg128, O, R>(p, tl, lds); break;
-      default: if constexpr (MASK & 16) tile_call<Cfg256, O, R>(p, tl, lds); break;
+      case 16: if constexpr (MASK & 1) tile_call<Pick<F8, Cfg16, Cfg16F>, O, R>(p, tl, lds); break;
+      case 32: if constexpr (MASK & 2) tile_call<Pick<F8, Cfg32, Cfg32F>, O, R>(p, tl, lds); break;
+      case 64: if constexpr (MASK & 4) tile_call<Pick<F8, Cfg64, Cfg64F>, O, R>(p, tl, lds); break;
+      case 128:
+        if constexpr (MASK & 8) tile_call<Pick<F8, Cfg128, Cfg128F>, O, R>(p, tl, lds);
+        break;
+      default:
+        if constexpr (MASK & 16) tile_call<Pick<F8, Cfg256, Cfg256F>, O, R>(p, tl, lds);
+        break;
     }
   }
 }
@@ -152,19 +164,25 @@ __global__ __launch_bounds__(kThreads) void tile_schedule_kernel(const int32_t *
   }
 }
 
-template <class C>
-constexpr int ring_bytes() { return C::LDS_BYTES; }
-
-template <int MASK>
+// Dynamic LDS a launch needs: the largest of the heights it compiles in.
+template <int MASK, bool F8>
 constexpr int lds_bytes() {
   int m = 0;
-  if (MASK & 1) m = m > ring_bytes<Cfg16>() ? m : ring_bytes<Cfg16>();
-  if (MASK & 2) m = m > ring_bytes<Cfg32>() ? m : ring_bytes<Cfg32>();
-  if (MASK & 4) m = m > ring_bytes<Cfg64>() ? m : ring_bytes<Cfg64>();
-  if (MASK & 8) m = m > ring_bytes<Cfg128>() ? m : ring_bytes<Cfg128>();
-  if (MASK & 16) m = m > ring_bytes<Cfg256>() ? m : ring_bytes<Cfg256>();
+  if (MASK & 1) m = m > Pick<F8, Cfg16, Cfg16F>::LDS_BYTES ? m : Pick<F8, Cfg16, Cfg16F>::LDS_BYTES;
+  if (MASK & 2) m = m > Pick<F8, Cfg32, Cfg32F>::LDS_BYTES ? m : Pick<F8, Cfg32, Cfg32F>::LDS_BYTES;
+  if (MASK & 4) m = m > Pick<F8, Cfg64, Cfg64F>::LDS_BYTES ? m : Pick<F8, Cfg64, Cfg64F>::LDS_BYTES;
+  if (MASK & 8)
+    m = m > Pick<F8, Cfg128, Cfg128F>::LDS_BYTES ? m : Pick<F8, Cfg128, Cfg128F>::LDS_BYTES;
+  if (MASK & 16)
+    m = m > Pick<F8, Cfg256, Cfg256F>::LDS_BYTES ? m : Pick<F8, Cfg256, Cfg256F>::LDS_BYTES;
   return m;
 }
+
+// Every launch's LDS (dynamic stages + the static schedule table) must fit
+// one CU's 160 KiB.
+constexpr int kLdsPerCu = 160 * 1024;
+static_assert(lds_bytes<31, false>() + (int)sizeof(SchedLds) <= kLdsPerCu, "LDS budget");
+static_assert(lds_bytes<31, true>() + (int)sizeof(SchedLds) <= kLdsPerCu, "LDS budget");
 
 // Per-device, per-variant launch limits (CU count x resident workgroups).
 struct LaunchInfo {
@@ -174,21 +192,21 @@ struct LaunchInfo {
 
 constexpr int kMaxDevices = 64;
 
-template <int MASK, Out O, Rows R>
+template <int MASK, Out O, Rows R, bool F8>
 static LaunchInfo launch_info(int dev) {
   static LaunchInfo cache[kMaxDevices];
   static std::once_flag once[kMaxDevices];
   std::call_once(once[dev], [dev]() {
     LaunchInfo li;
     int cus = 0, per_cu = 0;
-    const int lds = lds_bytes<MASK>();
+    const int lds = lds_bytes<MASK, F8>();
     li.err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (li.err == hipSuccess)
-      li.err = hipFuncSetAttribute((const void *)grouped_gemm_kernel<MASK, O, R>,
+      li.err = hipFuncSetAttribute((const void *)grouped_gemm_kernel<MASK, O, R, F8>,
                                    hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (li.err == hipSuccess)
       li.err = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &per_cu, (const void *)grouped_gemm_kernel<MASK, O, R>, kThreads, lds);
+          &per_cu, (const void *)grouped_gemm_kernel<MASK, O, R, F8>, kThreads, lds);
     if (li.err == hipSuccess) {
       if (per_cu < 1) per_cu = 1;
       li.grid = cus * per_cu;
@@ -200,16 +218,17 @@ static LaunchInfo launch_info(int dev) {
   return cache[dev];
 }
 
-template <int MASK, Out O, Rows R>
+template <int MASK, Out O, Rows R, bool F8>
 static gg_status_t launch(const Params &p, long long tile_bound, hipStream_t stream) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return GG_ERR_LAUNCH;
-  const LaunchInfo li = launch_info<MASK, O, R>(dev);
+  const LaunchInfo li = launch_info<MASK, O, R, F8>(dev);
   if (li.err != hipSuccess) return GG_ERR_LAUNCH;
   long long g = tile_bound < li.grid ? tile_bound : li.grid;
   g = (g + kXcds - 1) / kXcds * kXcds;  // keep a multiple of the XCD count
-  hipLaunchKernelGGL((grouped_gemm_kernel<MASK, O, R>), dim3((unsigned)g), dim3(kThreads),
-                     lds_bytes<MASK>(), stream, p);
+  constexpr int lds = lds_bytes<MASK, F8>();
+  hipLaunchKernelGGL((grouped_gemm_kernel<MASK, O, R, F8>), dim3((unsigned)g), dim3(kThreads),
+                     lds, stream, p);
   return hipGetLastError() == hipSuccess ? GG_OK : GG_ERR_LAUNCH;
 }
 
@@ -234,9 +253,9 @@ static gg_status_t check_sizes(const int32_t *off, int E, int N, int M_cap, int 
   return GG_OK;
 }
 
-// The product with C of element type O and rows of form R: argument checks,
-// then one launch. p arrives with every field but the sizes already set.
-template <Out O, Rows R>
+// The product with C of element type O, rows of form R and (F8) fp8 weights:
+// argument checks, then one launch.
+template <Out O, Rows R, bool F8 = false>
 static gg_status_t grouped_gemm(Params p, void *stream) {
   long long bound = 0;
   gg_status_t st = check_sizes(p.off, p.E, p.N, p.M_cap, p.bm_fixed, &bound);
@@ -254,22 +273,26 @@ static gg_status_t grouped_gemm(Params p, void *stream) {
     // the A resource covers all of X with 32-bit offsets
     if ((long long)p.n_src * p.K * 2 > (1LL << 31)) return GG_ERR_UNSUPPORTED;
   }
+  if constexpr (F8) {
+    if (p.b_scale == nullptr) return GG_ERR_INVALID_VALUE;
+    if (!aligned(p.b_scale, 16)) return GG_ERR_MISALIGNED;
+  }
   if (p.M_cap == 0 || bound == 0) return GG_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   switch (p.bm_fixed) {
-    case 16: return launch<1, O, R>(p, bound, s);
-    case 32: return launch<2, O, R>(p, bound, s);
-    case 64: return launch<4, O, R>(p, bound, s);
-    case 128: return launch<8, O, R>(p, bound, s);
-    case 256: return launch<16, O, R>(p, bound, s);
-    default: return launch<31, O, R>(p, bound, s);
+    case 16: return launch<1, O, R, F8>(p, bound, s);
+    case 32: return launch<2, O, R, F8>(p, bound, s);
+    case 64: return launch<4, O, R, F8>(p, bound, s);
+    case 128: return launch<8, O, R, F8>(p, bound, s);
+    case 256: return launch<16, O, R, F8>(p, bound, s);
+    default: return launch<31, O, R, F8>(p, bound, s);
   }
 }
 
 static Params make_params(const void *A, const void *B, const int32_t *off, void *C, int32_t E,
                           int32_t K, int32_t N, int32_t M_cap, int32_t bm) {
   return Params{static_cast<const uint16_t *>(A), static_cast<const uint16_t *>(B), off, C, E, K,
-                N, M_cap, bm, nullptr, nullptr, 0};
+                N, M_cap, bm, nullptr, nullptr, 0, nullptr};
 }
 
 }  // namespace gg
@@ -303,6 +326,15 @@ extern "C" gg_status_t gg_grouped_gemm_bf16_gather(const void *X, int32_t n_src,
   p.dst_rows = dst_rows;
   p.n_src = n_src;
   return grouped_gemm<Out::F32, Rows::Indexed>(p, stream);
+}
+
+extern "C" gg_status_t gg_grouped_gemm_fp8w(const void *A, const void *Bq, const float *b_scale,
+                                            const int32_t *group_offsets, float *C, int32_t E,
+                                            int32_t K, int32_t N, int32_t M_cap, int32_t bm,
+                                            void *stream) {
+  Params p = make_params(A, Bq, group_offsets, C, E, K, N, M_cap, bm);
+  p.b_scale = b_scale;
+  return grouped_gemm<Out::F32, Rows::Grouped, true>(p, stream);
 }
 
 extern "C" gg_status_t gg_tile_schedule(const int32_t *group_offsets, int32_t E, int32_t N,

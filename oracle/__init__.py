@@ -35,6 +35,13 @@ Contents
   product, then C[dst[r]] = C_grouped[r]. The permutation around the GEMM is
   the worklog's "What I am measuring" scope note; the indexed form is the
   plain reading of folding it into the loads and stores.
+* ``decode_e4m3`` / ``grouped_gemm_fp8w`` / ``grouped_gemm_fp8w_entries``:
+  the fp8-weight product C[r][n] = scale[e][n] * sum_k a[r][k] * dec(q[e][k][n])
+  with the OCP E4M3 decode written from the format's definition, and the sum
+  in binary64 (numpy float64 matmul per expert; the decoded weight times its
+  fp32 scale is exact in binary64). The Pearl Pulse article ("What the 15%
+  measures") mentions an FP8 scheme without details; per-output-column scales
+  are the reading taken.
 * ``round_to_bf16``: binary64 -> bfloat16 rounding to nearest, ties to even,
   written from the IEEE-754 definition of the format (8 significant bits,
   fp32's exponent range). It turns the fp64 reference into the bf16 values a
@@ -271,3 +278,66 @@ def round_to_bf16(x):
     out[nz] = r
     out[~np.isfinite(x)] = x[~np.isfinite(x)]
     return out
+
+
+def decode_e4m3(codes):
+    """OCP fp8 E4M3 codes (uint8) -> float64 values.
+
+    Bit 7 is the sign, bits 6..3 the exponent field (bias 7), bits 2..0 the
+    mantissa. Field 0: subnormal m/8 * 2^-6. Field 15 with mantissa 7: NaN
+    (E4M3 has no infinities). Otherwise (1 + m/8) * 2^(field - 7).
+    """
+    c = np.asarray(codes, dtype=np.int64)
+    sign = np.where(c >> 7, -1.0, 1.0)
+    f = (c >> 3) & 15
+    m = c & 7
+    mag = np.where(f == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.ldexp(1.0, f - 7))
+    out = sign * mag
+    out[(f == 15) & (m == 7)] = np.nan
+    return out
+
+
+def _fp8_expert_weights(Bq, scale, e):
+    return decode_e4m3(Bq[e]) * np.asarray(scale[e], dtype=np.float64)[None, :]
+
+
+def grouped_gemm_fp8w(A, Bq, scale, offsets, M_cap=None):
+    """fp64 fp8-weight grouped product. Returns (C, S), float64 [M_cap, N];
+    S[r][n] = sum_k |a[r][k] * dec(q[e][k][n]) * scale[e][n]|; rows outside
+    every group are NaN."""
+    A = np.asarray(A)
+    off = np.asarray(offsets, dtype=np.int64)
+    E, K, N = Bq.shape
+    M_cap = A.shape[0] if M_cap is None else int(M_cap)
+    C = np.full((M_cap, N), np.nan)
+    S = np.full((M_cap, N), np.nan)
+    for e in range(E):
+        r0, r1 = int(off[e]), int(off[e + 1])
+        if r1 <= r0:
+            continue
+        a = _bf16_to_f64(A[r0:r1])
+        w = _fp8_expert_weights(Bq, scale, e)
+        C[r0:r1] = a @ w
+        S[r0:r1] = np.abs(a) @ np.abs(w)
+    return C, S
+
+
+def grouped_gemm_fp8w_entries(A, Bq, scale, offsets, rows, cols):
+    """Selected entries of the fp8-weight product, one dot product each."""
+    off = np.asarray(offsets, dtype=np.int64)
+    rows = np.asarray(rows, dtype=np.int64)
+    cols = np.asarray(cols, dtype=np.int64)
+    c = np.empty(len(rows))
+    s = np.empty(len(rows))
+    for i, (r, n) in enumerate(zip(rows, cols)):
+        e = int(np.searchsorted(off, r, side="right") - 1)
+        a = _bf16_to_f64(A[r])
+        w = decode_e4m3(Bq[e, :, n]) * float(scale[e, n])
+        c[i] = a @ w
+        s[i] = np.abs(a) @ np.abs(w)
+    return c, s
+
+
+def _bf16_to_f64(bits):
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32).astype(np.float64)

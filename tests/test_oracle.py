@@ -369,3 +369,84 @@ def test_indexed_permutation_invariance():
     c0, _, _ = oracle.grouped_gemm(w.A, w.B, w.offsets)
     m = w.M_tot
     assert np.array_equal(c1[:m], c0[:m])
+
+
+def test_decode_e4m3_against_torch_and_definition():
+    torch = pytest.importorskip("torch")
+    codes = np.arange(256)
+    d = oracle.decode_e4m3(codes)
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    both_nan = np.isnan(d) & np.isnan(ref)
+    assert ((d == ref) | both_nan).all()
+    assert np.isnan(d[[0x7F, 0xFF]]).all() and np.isnan(d).sum() == 2
+    assert d[0x7E] == 448.0 and d[0xFE] == -448.0     # largest finite
+    assert d[0x38] == 1.0 and d[0xB8] == -1.0
+    assert d[0x01] == 2.0 ** -9 and d[0x08] == 2.0 ** -6  # smallest subnormal / normal
+
+
+def _int_codes(vals):
+    # E4M3 codes of small integers: 1 = 0x38, 2 = 0x40, 3 = 0x44, sign in bit 7
+    table = {0: 0x00, 1: 0x38, 2: 0x40, 3: 0x44}
+    v = np.asarray(vals)
+    return (np.vectorize(table.get)(np.abs(v)) | ((v < 0) << 7)).astype(np.uint8)
+
+
+def test_fp8w_brute_force_integers():
+    rng = np.random.default_rng(35)
+    E, K, N = 3, 7, 5
+    sizes = [2, 0, 4]
+    off = wl.offsets_from_sizes(sizes)
+    A = wl.f32_to_bf16_bits(rng.integers(-3, 4, size=(6, K)).astype(np.float32))
+    qv = rng.integers(-3, 4, size=(E, K, N))
+    Bq = _int_codes(qv)
+    scale = np.ldexp(1.0, rng.integers(-3, 4, size=(E, N))).astype(np.float32)
+    c, s = oracle.grouped_gemm_fp8w(A, Bq, scale, off)
+    af = wl.bf16_bits_to_f32(A)
+    for e in range(E):
+        for r in range(off[e], off[e + 1]):
+            for n in range(N):
+                acc = 0.0
+                for k in range(K):
+                    acc += float(af[r, k]) * float(qv[e, k, n])
+                assert c[r, n] == acc * float(scale[e, n])
+
+
+def test_fp8w_unit_scale_reduces_to_bf16_product():
+    # every E4M3 value is a bf16 value, so with unit scales the fp8-weight
+    # product is the bf16 grouped product of the decoded weights
+    w = wl.make_workload(E=3, K=96, N=40, sizes=[9, 4, 0], seed=36)
+    rng = np.random.default_rng(37)
+    Bq = rng.integers(0, 256, size=(3, 96, 40)).astype(np.uint8)
+    Bq[(Bq & 0x7F) == 0x7F] = 0x3C  # no NaN codes
+    ones = np.ones((3, 40), dtype=np.float32)
+    c, s = oracle.grouped_gemm_fp8w(w.A, Bq, ones, w.offsets)
+    Bbf = wl.f32_to_bf16_bits(oracle.decode_e4m3(Bq).astype(np.float32))
+    c0, s0, _ = oracle.grouped_gemm(w.A, Bbf, w.offsets)
+    m = w.M_tot
+    assert np.allclose(c[:m], c0[:m], rtol=0, atol=1e-12 * s0[:m].max())
+    assert np.allclose(s[:m], s0[:m], rtol=1e-14)
+
+
+def test_fp8w_column_scale_is_linear_and_entries_match():
+    w = wl.make_workload(E=2, K=64, N=24, sizes=[5, 7], seed=38)
+    q, scale = wl.fp8_weights(w)
+    c, _ = oracle.grouped_gemm_fp8w(w.A, q, scale, w.offsets)
+    scale2 = scale.copy()
+    scale2[:, 3] *= 2
+    c2, _ = oracle.grouped_gemm_fp8w(w.A, q, scale2, w.offsets)
+    assert np.array_equal(c2[:, 3], 2 * c[:, 3])
+    rows = np.arange(w.M_tot).repeat(3)
+    cols = np.tile([0, 11, 23], w.M_tot)
+    ce, _ = oracle.grouped_gemm_fp8w_entries(w.A, q, scale, w.offsets, rows, cols)
+    assert np.allclose(ce, c[rows, cols], rtol=1e-14, atol=1e-14)
+
+
+def test_fp8_weight_recipe_is_close_to_bf16_weights():
+    # the input recipe: per-column scale maps the largest |w| to 448, and the
+    # quantized weight is within half an E4M3 spacing (2^-4 relative) of it
+    w = wl.make_workload(E=2, K=128, N=32, sizes=[1, 1], seed=39)
+    q, scale = wl.fp8_weights(w)
+    b = wl.bf16_bits_to_f32(w.B).astype(np.float64)
+    deq = oracle.decode_e4m3(q) * scale[:, None, :]
+    assert (np.abs(oracle.decode_e4m3(q)).max(axis=1) == 448.0).all()
+    assert (np.abs(deq - b) <= 2.0 ** -4 * np.abs(b) + 2.0 ** -10 * scale[:, None, :]).all()

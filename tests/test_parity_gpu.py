@@ -478,3 +478,97 @@ def test_gather_decode_shape_sampled(gg):
     got = out[dst[r], cols]
     d = np.abs(got - c)
     assert (d <= parity.ELEM * s).all()
+
+
+# ---- fp8 weights with per-column scales ---------------------------------------------
+
+def _fp8_dev(w, Bq, scale):
+    dev = torch.device("cuda:0")
+    A = torch.from_numpy(w.A.view(np.int16)).to(dev).view(torch.bfloat16)
+    return (A, torch.from_numpy(Bq).to(dev), torch.from_numpy(scale).to(dev),
+            torch.from_numpy(w.offsets).to(dev))
+
+
+def _fp8_compare(gg, w, Bq, scale, bm, what):
+    A, Bd, sd, off = _fp8_dev(w, Bq, scale)
+    C = torch.full((w.M_cap, w.N), float("nan"), dtype=torch.float32, device="cuda:0")
+    _say("case fp8w %s E=%d K=%d N=%d M_tot=%d bm=%d" % (what, w.E, w.K, w.N, w.M_tot, bm))
+    gg.grouped_gemm_fp8w(A, Bd, sd, off, out=C, bm=bm)
+    torch.cuda.synchronize()
+    got = C.cpu().numpy()
+    ref, s = oracle.grouped_gemm_fp8w(w.A, Bq, scale, w.offsets, M_cap=w.M_cap)
+    m = w.M_tot
+    parity.check(got[:m], ref[:m], s[:m], what)
+    assert np.isnan(got[m:]).all()
+    return got
+
+
+@pytest.mark.parametrize("bm", BMS)
+def test_fp8w_ragged_wide(gg, bm):
+    w = wl.make_workload(E=4, K=200, N=776, sizes=[300, 0, 45, 517], seed=27, M_cap=870)
+    Bq, scale = wl.fp8_weights(w)
+    _fp8_compare(gg, w, Bq, scale, bm, "fp8w ragged-wide")
+
+
+@pytest.mark.parametrize("bm", [0, 16, 128])
+def test_fp8w_tiny_all_codes(gg, bm):
+    # every finite E4M3 code (subnormals included) appears in the weights
+    w = wl.make_workload("tiny")
+    rng = np.random.default_rng(47)
+    Bq = rng.integers(0, 256, size=(w.E, w.K, w.N)).astype(np.uint8)
+    Bq[(Bq & 0x7F) == 0x7F] = 0x01
+    scale = rng.uniform(0.5, 2.0, size=(w.E, w.N)).astype(np.float32)
+    _fp8_compare(gg, w, Bq, scale, bm, "fp8w tiny")
+
+
+@pytest.mark.parametrize("bm", [0, 64])
+def test_fp8w_integer_exact(gg, bm):
+    # integer activations and weights, power-of-two scales: exact in fp32
+    w = wl.make_workload(E=5, K=512, N=264, sizes=[5, 0, 40, 129, 16], seed=22, values="int")
+    rng = np.random.default_rng(48)
+    table = np.array([0x00, 0x38, 0x40, 0x44], dtype=np.uint8)  # 0, 1, 2, 3
+    v = rng.integers(-3, 4, size=(w.E, w.K, w.N))
+    Bq = (table[np.abs(v)] | ((v < 0).astype(np.uint8) << 7)).astype(np.uint8)
+    scale = np.ldexp(1.0, rng.integers(-2, 3, size=(w.E, w.N))).astype(np.float32)
+    A, Bd, sd, off = _fp8_dev(w, Bq, scale)
+    _say("case fp8w int-exact bm=%d" % bm)
+    got = gg.grouped_gemm_fp8w(A, Bd, sd, off, bm=bm).cpu().numpy()
+    ref, _ = oracle.grouped_gemm_fp8w(w.A, Bq, scale, w.offsets)
+    m = w.M_tot
+    assert (got[:m] == ref[:m]).all()
+
+
+def test_fp8w_unit_scale_equals_bf16_path(gg):
+    # with unit scales, the fp8 path is the bf16 path on the decoded weights
+    # (the widening to bf16 is exact and the K order is the same)
+    w = wl.make_workload(E=6, K=328, N=392, sizes=[0, 1, 17, 130, 0, 300], seed=21, M_cap=470)
+    Bq, _ = wl.fp8_weights(w)
+    ones = np.ones((w.E, w.N), dtype=np.float32)
+    A, Bd, sd, off = _fp8_dev(w, Bq, ones)
+    _say("case fp8w unit scale vs bf16 path")
+    c8 = gg.grouped_gemm_fp8w(A, Bd, sd, off, bm=0)
+    Bbf = wl.f32_to_bf16_bits(oracle.decode_e4m3(Bq).astype(np.float32))
+    Bb = torch.from_numpy(Bbf.view(np.int16)).cuda().view(torch.bfloat16)
+    c16 = gg.grouped_gemm(A, Bb, off, bm=0)
+    torch.cuda.synchronize()
+    m = w.M_tot
+    assert torch.equal(c8[:m], c16[:m])
+
+
+def test_fp8w_decode_shape_sampled(gg):
+    w = _full("decode")
+    _say("case fp8w decode: quantizing weights")
+    Bq, scale = wl.fp8_weights(w)
+    A, Bd, sd, off = _fp8_dev(w, Bq, scale)
+    C = torch.full((w.M_cap + 8, w.N), float("nan"), dtype=torch.float32, device="cuda:0")
+    _say("case fp8w decode shape")
+    gg.grouped_gemm_fp8w(A, Bd, sd, off, out=C[: w.M_cap], bm=0)
+    torch.cuda.synchronize()
+    out = C.cpu().numpy()
+    assert np.isfinite(out[: w.M_tot]).all() and np.isnan(out[w.M_cap:]).all()
+    rng = np.random.default_rng(10)
+    rows = rng.integers(0, w.M_tot, size=1500)
+    cols = rng.integers(0, w.N, size=1500)
+    c, s = oracle.grouped_gemm_fp8w_entries(w.A, Bq, scale, w.offsets, rows, cols)
+    d = np.abs(out[rows, cols] - c)
+    assert (d <= parity.ELEM * s).all()

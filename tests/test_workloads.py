@@ -44,3 +44,13 @@ def test_deterministic_draws():
     # values have the stated scale: N(0,1)/sqrt(256)
     v = wl.bf16_bits_to_f32(a.B)
     assert abs(float(v.std()) - 1 / 16) < 0.002
+
+
+def test_e4m3_rounding_matches_torch():
+    rng = np.random.default_rng(5)
+    x = np.concatenate([rng.standard_normal(50000).astype(np.float32) * s for s in (1e-3, 0.1, 3, 100)])
+    x = x[np.abs(x) <= 448]
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert (wl.f32_to_e4m3_bits(x) == ref).all()
+    # saturation above the largest finite value
+    assert (wl.f32_to_e4m3_bits(np.array([500.0, -1e6], dtype=np.float32)) == [0x7E, 0xFE]).all()

@@ -20,6 +20,13 @@ What is drawn, and why it looks like the pages' workloads:
   the top 16 bits of an IEEE binary32 word; the rounding below is the
   textbook round-half-even on the 16 discarded bits (inputs are finite).
 
+* fp8 weights. ``fp8_weights`` turns a workload's bf16 weights into OCP fp8
+  E4M3 codes with one fp32 scale per expert and output column: the scale
+  maps the column's largest magnitude to 448 (the largest finite E4M3 value)
+  and every weight divided by it is rounded to the nearest E4M3 value, ties
+  to even. This is the input recipe of the fp8-weight product, not part of
+  the product itself.
+
 Streams: the group sizes come from numpy's PCG64 generator seeded with the
 workload seed; A from ``default_rng([seed, 1])``; expert e's weight slice
 from ``default_rng([seed, 2, e])``. Giving every expert its own stream keeps
@@ -46,6 +53,8 @@ __all__ = [
     "offsets_from_sizes",
     "make_workload",
     "config_sizes",
+    "f32_to_e4m3_bits",
+    "fp8_weights",
 ]
 
 
@@ -217,3 +226,55 @@ def make_workload(name: str = None, *, E=None, K=None, N=None, sizes=None, scale
         list(ex.map(draw_expert, range(E)))
     return Workload(name=name or "custom", E=E, K=K, N=N, sizes=sizes, offsets=off,
                     M_cap=M_cap, A=A, B=B, seed=seed)
+
+
+def f32_to_e4m3_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to OCP fp8 E4M3 codes (uint8): nearest, ties to even,
+    magnitudes above 448 saturated to 448.
+
+    E4M3: 1 sign bit, 4 exponent bits (bias 7), 3 mantissa bits; normal values
+    (1 + m/8) * 2^(e-7) for exponent fields 1..15 (field 15 with m = 7 is NaN,
+    so the largest finite value is 1.75 * 2^8 = 448); subnormals m/8 * 2^-6.
+    Values in [2^p, 2^(p+1)) are spaced 2^(p-3) apart, and below 2^-6 the
+    spacing stays 2^-9. Scaling by powers of two is exact in binary64, so the
+    division by the spacing is exact and numpy's round applies the tie rule.
+    """
+    x = np.asarray(x, dtype=np.float32).astype(np.float64)
+    neg = np.signbit(x)
+    a = np.abs(x)
+    _, ex = np.frexp(a)                       # a = f * 2^ex, f in [0.5, 1)
+    spacing = np.ldexp(1.0, np.maximum(ex - 1, -6) - 3)
+    q = np.minimum(np.round(a / spacing) * spacing, 448.0)
+    code = np.zeros(a.shape, dtype=np.int64)
+    normal = q >= 2.0 ** -6
+    _, eq = np.frexp(q[normal])
+    p = eq - 1                                # q = (1 + m/8) * 2^p
+    m = np.round(np.ldexp(q[normal], -p) * 8).astype(np.int64) - 8
+    code[normal] = ((p + 7) << 3) | m
+    code[~normal] = np.round(q[~normal] / 2.0 ** -9).astype(np.int64)
+    code |= neg.astype(np.int64) << 7
+    return code.astype(np.uint8)
+
+
+def fp8_weights(w: "Workload"):
+    """fp8 E4M3 codes and per-(expert, column) fp32 scales for w.B.
+
+    scale[e, n] = max_k |B[e, k, n]| / 448 (1 for an all-zero column), computed
+    in float32; codes = E4M3 rounding of B[e, k, n] / scale[e, n] (float32
+    division). Returns (codes uint8 [E, K, N], scale float32 [E, N]).
+    """
+    E, K, N = w.B.shape
+    codes = np.empty((E, K, N), dtype=np.uint8)
+    scale = np.empty((E, N), dtype=np.float32)
+
+    def one(e):
+        b = bf16_bits_to_f32(w.B[e])
+        s_e = (np.abs(b).max(axis=0) / np.float32(448.0)).astype(np.float32)
+        s_e[s_e == 0] = 1.0
+        scale[e] = s_e
+        codes[e] = f32_to_e4m3_bits(b / s_e)
+
+    workers = max(1, min(8, os.cpu_count() or 1, E))
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        list(ex.map(one, range(E)))
+    return codes, scale

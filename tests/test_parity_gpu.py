@@ -572,3 +572,16 @@ def test_fp8w_decode_shape_sampled(gg):
     c, s = oracle.grouped_gemm_fp8w_entries(w.A, Bq, scale, w.offsets, rows, cols)
     d = np.abs(out[rows, cols] - c)
     assert (d <= parity.ELEM * s).all()
+
+
+# ---- several tiles per workgroup (the pipelined tile loop) -----------------------------
+
+@pytest.mark.parametrize("bm", BMS)
+@pytest.mark.parametrize("K", [64, 200])
+def test_many_tiles_per_workgroup(gg, bm, K):
+    # 8 experts x ~700 rows x 16 column tiles: hundreds to thousands of tiles,
+    # so every workgroup runs several tiles of one height back to back (the
+    # next tile's first slices are loaded while the current one is stored);
+    # K = 64 is a single slice, K = 200 ends inside the fourth
+    w = wl.make_workload(E=8, K=K, N=4096, sizes=[700, 690, 0, 705, 1, 650, 700, 33], seed=49)
+    _full_compare(gg, w, bm, "many-tiles K=%d" % K)

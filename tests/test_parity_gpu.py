@@ -585,3 +585,62 @@ def test_many_tiles_per_workgroup(gg, bm, K):
     # K = 64 is a single slice, K = 200 ends inside the fourth
     w = wl.make_workload(E=8, K=K, N=4096, sizes=[700, 690, 0, 705, 1, 650, 700, 33], seed=49)
     _full_compare(gg, w, bm, "many-tiles K=%d" % K)
+
+
+# ---- capture in a HIP graph -------------------------------------------------------------
+
+def test_graph_capture_replays(gg):
+    # the entry point enqueues one kernel, allocates nothing and never syncs,
+    # so it can be captured; every replay must reproduce the eager result,
+    # with eager work and synchronisation between replays
+    w = wl.make_workload(E=6, K=328, N=392, sizes=[0, 1, 17, 130, 0, 300], seed=21, M_cap=470)
+    A, B, off = _dev(w)
+    eager = gg.grouped_gemm(A, B, off, bm=0)
+    torch.cuda.synchronize()
+    C = torch.full_like(eager, float("nan"))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    _say("case graph capture")
+    with torch.cuda.graph(g, stream=s):
+        gg.grouped_gemm(A, B, off, out=C, bm=0)
+    torch.cuda.synchronize()
+    m = w.M_tot
+    for i in range(4):
+        C.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(C[:m], eager[:m]), "replay %d" % i
+        assert torch.isnan(C[m:]).all()
+        junk = torch.randn(1 << 20, device="cuda:0").sum()  # eager work between replays
+        torch.cuda.synchronize()
+
+
+# ---- edge shapes ---------------------------------------------------------------------
+
+@pytest.mark.parametrize("bm", [0, 16, 256])
+@pytest.mark.parametrize("shape", [
+    dict(E=1, K=8, N=8, sizes=[5]),                       # smallest K and N
+    dict(E=3, K=16, N=24, sizes=[1, 2, 3]),               # tile far wider than N
+    dict(E=2, K=8, N=520, sizes=[300, 1]),                # one K slice, 8 columns past 512
+])
+def test_edge_shapes(gg, bm, shape):
+    w = wl.make_workload(seed=50, **shape)
+    _full_compare(gg, w, bm, "edge %s" % shape)
+
+
+@pytest.mark.parametrize("bm", [0, 32])
+def test_max_experts(gg, bm):
+    # 1024 experts (the LDS table full), 0-3 rows each
+    rng = np.random.default_rng(51)
+    sizes = [int(x) for x in rng.integers(0, 4, size=1024)]
+    w = wl.make_workload(E=1024, K=64, N=64, sizes=sizes, seed=51)
+    _full_compare(gg, w, bm, "E=1024")
+
+
+def test_large_m_cap_few_rows(gg):
+    # M_cap far above the routed rows: the grid bound comes from M_cap, the
+    # tiles from the offsets; rows past off[E] stay untouched
+    w = wl.make_workload(E=4, K=96, N=136, sizes=[3, 0, 40, 2], seed=52, M_cap=200000)
+    _full_compare(gg, w, 0, "M_cap=200000")

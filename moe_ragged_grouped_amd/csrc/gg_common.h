@@ -61,9 +61,15 @@ __device__ __forceinline__ buf_rsrc make_buf(const void *base, uint32_t bytes) {
                                            kBufWord3);
 }
 
+// Cache-policy operand of a buffer access (gfx950): nt marks the data as
+// streaming, so it does not displace lines that other tiles will reuse.
+constexpr int kCacheDefault = 0;
+constexpr int kCacheStream = 2;  // nt
+
 // One 16-byte load at base + voff + soff; zeros when the offset is out of range.
+template <int POLICY = kCacheDefault>
 __device__ __forceinline__ u32x4 ld_buf16(buf_rsrc r, uint32_t voff, uint32_t soff) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, POLICY);
 }
 
 // One 4-byte global load of an index (global_load_dword).

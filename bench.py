@@ -19,10 +19,14 @@ Prints one JSON line:
              sources, else null.
   cpu_baseline  the CPU oracle timed on a bounded sample of the same workload.
 
-    python bench.py [--steps K] [--warmup W] [--config decode] [--bm 0] [--out fp32|bf16]
+    python bench.py [--steps K] [--warmup W] [--config decode] [--bm 0]
+                    [--out fp32|bf16|swiglu]
 
 --out bf16 times the bf16-output entry point (C rounded to bf16 in the
-epilogue); its algorithmic bytes count C at 2 bytes per element.
+epilogue); its algorithmic bytes count C at 2 bytes per element. --out swiglu
+times the fused gate/up entry point (B's columns read as interleaved gate and
+up pairs, bf16 H of N/2 columns written); its output counts at 1 byte per
+product column.
 """
 
 import argparse
@@ -120,8 +124,9 @@ def main():
     ap.add_argument("--ramp-ms", type=float, default=300.0,
                     help="untimed launches for at least this long before the warmup steps, so "
                          "the GPU clocks have left their idle state when timing starts")
-    ap.add_argument("--out", default="fp32", choices=("fp32", "bf16"),
-                    help="element type of C (bf16: rounded in the epilogue)")
+    ap.add_argument("--out", default="fp32", choices=("fp32", "bf16", "swiglu"),
+                    help="what the epilogue writes: fp32 C, bf16 C, or bf16 SwiGLU of "
+                         "(gate, up) column pairs")
     ap.add_argument("--weights", default="bf16", choices=("bf16", "fp8"),
                     help="fp8: E4M3 weights with per-column scales (a separate precision)")
     ap.add_argument("--gather", action="store_true",
@@ -163,7 +168,8 @@ def main():
     B = torch.from_numpy(w.B.view(np.int16)).to(dev).view(torch.bfloat16)
     off = torch.from_numpy(w.offsets).to(dev)
     c_dtype = torch.float32 if args.out == "fp32" else torch.bfloat16
-    C = torch.empty((w.M_cap, w.N), dtype=c_dtype, device=dev)
+    C = torch.empty((w.M_cap, w.N // 2 if args.out == "swiglu" else w.N), dtype=c_dtype,
+                    device=dev)
     if args.weights == "fp8":
         # fp8 E4M3 weights with per-(expert, column) fp32 scales, quantized
         # from the bf16 weights on the host (input recipe, untimed)
@@ -189,6 +195,8 @@ def main():
             gg.grouped_gemm_fp8w(A, Bq, Bs, off, out=C, bm=args.bm)
         elif args.gather:
             gg.grouped_gemm_gather(X, perm, B, off, dst_rows=perm, out=C, bm=args.bm)
+        elif args.out == "swiglu":
+            gg.grouped_gemm_swiglu(A, B, off, out=C, bm=args.bm)
         else:
             gg.grouped_gemm(A, B, off, out=C, bm=args.bm)
     torch.cuda.synchronize()
@@ -227,7 +235,7 @@ def main():
     launch_s = ev_s / args.steps                # average launch on the stream
 
     useful = 2.0 * w.M_tot * w.K * w.N
-    c_bytes = 4 if args.out == "fp32" else 2
+    c_bytes = {"fp32": 4, "bf16": 2, "swiglu": 1}[args.out]  # per product column
     active = int((w.sizes > 0).sum())
     b_bytes = 2 * w.K * w.N * active if args.weights == "bf16" else (w.K + 4) * w.N * active
     alg_bytes = (2 * w.M_tot * w.K + b_bytes + c_bytes * w.M_tot * w.N

@@ -101,6 +101,33 @@ gg_status_t gg_grouped_gemm_bf16_bf16out(const void *A, const void *B,
                                          void *stream);
 
 /*
+ * gg_grouped_gemm_bf16_swiglu -- the gate and up projections with the SwiGLU
+ * activation applied in the epilogue.
+ *
+ * The Pearl Pulse article ("What the 15% measures") benchmarks the kernel on
+ * the gate and up projections of MoE models; the activation between them
+ * and the next projection is silu(gate) * up. Here B holds both projections
+ * with their columns interleaved, so the product's two columns of one output
+ * are computed by the same lane and need no exchange:
+ *   B   bf16 [E][K][N], N = 2 * I: column 2j is gate column j and column
+ *       2j+1 is up column j (a caller holding [W_gate | W_up] interleaves
+ *       the columns once, when the weights are loaded).
+ *   H   bf16 [M_cap][N/2], row-major, 16-byte aligned:
+ *       H[r][j] = silu(C[r][2j]) * C[r][2j+1], silu(x) = x / (1 + e^-x),
+ *       where C is the fp32 product gg_grouped_gemm_bf16 computes for the
+ *       same inputs. The activation is evaluated in fp32 (an accurate expf
+ *       and an IEEE division) and rounded once to the nearest bf16 (ties to
+ *       even). Rows at or past off[E] are not written.
+ * A, group_offsets, E, K, N, M_cap, bm, the stream, the status codes and
+ * the conditions for them are those of gg_grouped_gemm_bf16 (N a multiple
+ * of 8, so I is a multiple of 4).
+ */
+gg_status_t gg_grouped_gemm_bf16_swiglu(const void *A, const void *B,
+                                        const int32_t *group_offsets, void *H, int32_t E,
+                                        int32_t K, int32_t N, int32_t M_cap, int32_t bm,
+                                        void *stream);
+
+/*
  * gg_grouped_gemm_bf16_gather -- the product with the expert grouping done by
  * index instead of by copying rows (the worklog's "What I am measuring" puts
  * the token permutation on either side of the grouped GEMM; here it is folded

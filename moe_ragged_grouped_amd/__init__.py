@@ -14,7 +14,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["grouped_gemm", "grouped_gemm_gather", "grouped_gemm_fp8w", "tile_schedule", "library_path", "load_library", "GroupedGemmError",
+__all__ = ["grouped_gemm", "grouped_gemm_swiglu", "grouped_gemm_gather", "grouped_gemm_fp8w", "tile_schedule", "library_path", "load_library", "GroupedGemmError",
            "BM_CHOICES", "TILE_N", "TILE_WIDTH", "MAX_EXPERTS", "SYMBOLS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -24,8 +24,9 @@ BM_CHOICES = (16, 32, 64, 128, 256)
 TILE_N = 256                      # tile width (every height)
 TILE_WIDTH = {h: TILE_N for h in BM_CHOICES}  # per tile height
 MAX_EXPERTS = 1024
-SYMBOLS = ("gg_grouped_gemm_bf16", "gg_grouped_gemm_bf16_bf16out", "gg_grouped_gemm_bf16_gather",
-           "gg_grouped_gemm_fp8w", "gg_tile_schedule", "gg_status_string")
+SYMBOLS = ("gg_grouped_gemm_bf16", "gg_grouped_gemm_bf16_bf16out", "gg_grouped_gemm_bf16_swiglu",
+           "gg_grouped_gemm_bf16_gather", "gg_grouped_gemm_fp8w", "gg_tile_schedule",
+           "gg_status_string")
 
 _lib = None
 
@@ -51,6 +52,8 @@ def load_library():
         lib.gg_grouped_gemm_bf16.restype = ctypes.c_int
         lib.gg_grouped_gemm_bf16_bf16out.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
         lib.gg_grouped_gemm_bf16_bf16out.restype = ctypes.c_int
+        lib.gg_grouped_gemm_bf16_swiglu.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
+        lib.gg_grouped_gemm_bf16_swiglu.restype = ctypes.c_int
         lib.gg_grouped_gemm_bf16_gather.argtypes = [vp, i32, vp, vp, vp, vp, vp, i32, i32, i32, i32,
                                                     i32, vp]
         lib.gg_grouped_gemm_bf16_gather.restype = ctypes.c_int
@@ -77,18 +80,10 @@ def _stream_handle(device, stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def grouped_gemm(A, B, offsets, out=None, bm: int = 0, stream=None, out_dtype=None):
-    """C[off[e]:off[e+1]] = A[off[e]:off[e+1]] @ B[e] for every expert e, in one launch.
-
-    A: bf16 [M_cap, K]; B: bf16 [E, K, N]; offsets: int32 [E+1] (device);
-    out: optional fp32 or bf16 [M_cap, N] (out_dtype, default fp32, when out
-    is not given); bm: 0 (per-expert choice on the device) or
-    16/32/64/128/256. A bf16 ``out`` receives the fp32 result rounded to
-    nearest even. Rows of ``out`` at or past offsets[E] are left as they
-    were. Enqueued on ``stream`` (default: torch's current stream).
-    """
+def _grouped_args(A, B, offsets):
+    """Checks A bf16 [M_cap, K], B bf16 [E, K, N], offsets int32 [E+1] (device,
+    contiguous); returns E, K, N, M_cap."""
     import torch
-    lib = load_library()
     if A.dtype != torch.bfloat16 or B.dtype != torch.bfloat16:
         raise TypeError("A and B must be bfloat16")
     if offsets.dtype != torch.int32:
@@ -104,6 +99,22 @@ def grouped_gemm(A, B, offsets, out=None, bm: int = 0, stream=None, out_dtype=No
     if A.shape[1] != K or offsets.shape[0] != E + 1:
         raise ValueError("shape mismatch: A %s, B %s, offsets %s" % (tuple(A.shape), tuple(B.shape),
                                                                       tuple(offsets.shape)))
+    return E, K, N, M_cap
+
+
+def grouped_gemm(A, B, offsets, out=None, bm: int = 0, stream=None, out_dtype=None):
+    """C[off[e]:off[e+1]] = A[off[e]:off[e+1]] @ B[e] for every expert e, in one launch.
+
+    A: bf16 [M_cap, K]; B: bf16 [E, K, N]; offsets: int32 [E+1] (device);
+    out: optional fp32 or bf16 [M_cap, N] (out_dtype, default fp32, when out
+    is not given); bm: 0 (per-expert choice on the device) or
+    16/32/64/128/256. A bf16 ``out`` receives the fp32 result rounded to
+    nearest even. Rows of ``out`` at or past offsets[E] are left as they
+    were. Enqueued on ``stream`` (default: torch's current stream).
+    """
+    import torch
+    lib = load_library()
+    E, K, N, M_cap = _grouped_args(A, B, offsets)
     if out is None:
         dt = torch.float32 if out_dtype is None else out_dtype
         if dt not in (torch.float32, torch.bfloat16):
@@ -116,6 +127,30 @@ def grouped_gemm(A, B, offsets, out=None, bm: int = 0, stream=None, out_dtype=No
     st = fn(A.data_ptr(), B.data_ptr(), offsets.data_ptr(), out.data_ptr(), E, K, N, M_cap, int(bm),
             _stream_handle(A.device, stream))
     _check(st, fn.__name__)
+    return out
+
+
+def grouped_gemm_swiglu(A, B, offsets, out=None, bm: int = 0, stream=None):
+    """H[r, j] = silu(C[r, 2j]) * C[r, 2j+1] for C = the grouped product, in one launch.
+
+    A, B, offsets, bm and stream as in grouped_gemm; B's columns hold the
+    gate and up projections interleaved (column 2j gate j, column 2j+1 up j).
+    out: optional bf16 [M_cap, N // 2]. The activation runs in fp32 in the
+    kernel's epilogue and is rounded once to bf16. Rows at or past
+    offsets[E] are left as they were.
+    """
+    import torch
+    lib = load_library()
+    E, K, N, M_cap = _grouped_args(A, B, offsets)
+    if out is None:
+        out = torch.empty((M_cap, N // 2), dtype=torch.bfloat16, device=A.device)
+    elif (out.dtype != torch.bfloat16 or tuple(out.shape) != (M_cap, N // 2)
+          or not out.is_contiguous()):
+        raise ValueError("out must be a contiguous bf16 [M_cap, N // 2] tensor")
+    st = lib.gg_grouped_gemm_bf16_swiglu(A.data_ptr(), B.data_ptr(), offsets.data_ptr(),
+                                         out.data_ptr(), E, K, N, M_cap, int(bm),
+                                         _stream_handle(A.device, stream))
+    _check(st, "gg_grouped_gemm_bf16_swiglu")
     return out
 
 

@@ -99,8 +99,9 @@ __device__ __forceinline__ void fp8x16_to_bf16x16(u32x4 in, u32x4 &lo, u32x4 &hi
 // One 16-byte global store (global_store_dwordx4).
 __device__ __forceinline__ void st_g16(float *p, f32x4 v) { *(gbl_f32x4 *)p = v; }
 
-// Output element types of the epilogue.
-enum class Out { F32, BF16 };
+// What the epilogue writes: C in fp32, C rounded to bf16, or the SwiGLU of
+// interleaved (gate, up) column pairs rounded to bf16 (half as many columns).
+enum class Out { F32, BF16, SwiGluBF16 };
 
 typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
 typedef __attribute__((address_space(1))) bf16x4 gbl_bf16x4;
@@ -109,6 +110,19 @@ typedef __attribute__((address_space(1))) bf16x4 gbl_bf16x4;
 // and stored as one 8-byte global store.
 __device__ __forceinline__ void st_g8_bf16(uint16_t *p, f32x4 v) {
   *(gbl_bf16x4 *)p = __builtin_convertvector(v, bf16x4);
+}
+
+// SwiGLU of one lane's four columns, taken as two (gate, up) pairs:
+// v = (g0, u0, g1, u1) -> silu(g0) * u0, silu(g1) * u1 with
+// silu(x) = x / (1 + e^-x), evaluated in fp32 (accurate expf, IEEE division;
+// e^-x overflows to infinity for very negative x, giving -0), each rounded
+// once to bf16 (ties to even) and stored as one 4-byte global store.
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((address_space(1))) bf16x2 gbl_bf16x2;
+__device__ __forceinline__ float silu(float x) { return x / (1.0f + expf(-x)); }
+__device__ __forceinline__ void st_g4_swiglu_bf16(uint16_t *p, f32x4 v) {
+  const f32x2 h = {silu(v.x) * v.y, silu(v.z) * v.w};
+  *(gbl_bf16x2 *)p = __builtin_convertvector(h, bf16x2);
 }
 
 // Transposing LDS read of a 4 (rows) x 16 (16-bit columns) block per 16-lane

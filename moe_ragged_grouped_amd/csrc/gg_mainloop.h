@@ -95,7 +95,8 @@ enum class Rows { Grouped, Indexed };
 struct TileArgs {
   const uint16_t *A;   // Grouped: A rows of this tile (row r at A + r * K); Indexed: X
   const char *B;       // B[e] + col0: element (k, n) at byte (k * N + n) * B_ELEM
-  void *C;             // C + row0 * N + col0 (C + col0 when dst is given), fp32 or bf16
+  void *C;             // C + row0 * N + col0 (C + col0 when dst is given); for SwiGLU
+                       // output H + row0 * N/2 + col0/2
   int rows, K, N, ncols;  // ncols = valid columns in this tile (<= BN)
   long long b_bytes;   // bytes from B to the end of B[e]: (K * N - col0) * B_ELEM
   const float *scale;  // fp8 B: scale[e][col0 ..], one per output column; else null
@@ -263,8 +264,9 @@ __device__ __forceinline__ void mma_stage(f32x4 (&acc)[C::NI][C::MI], const lds_
 
 // Full K loop and epilogue for one tile. lds must hold C::LDS_BYTES. Ends with
 // a workgroup barrier, so the next tile may refill the stages at once. O is
-// the element type of C: fp32 (the accumulators as they are) or bf16 (rounded
-// to nearest even in the epilogue). R says where rows come from and go.
+// what the epilogue writes: fp32 C (the accumulators as they are), bf16 C
+// (rounded to nearest even), or bf16 SwiGLU of (gate, up) column pairs into
+// an output N/2 columns wide. R says where rows come from and go.
 template <class C, Out O, Rows R>
 __device__ __forceinline__ void run_tile(const TileArgs &t, lds_u16 *lds) {
   lds_u16 *const As0 = lds;                       // stage s: As0 + s * A_STAGE
@@ -353,8 +355,10 @@ __device__ __forceinline__ void run_tile(const TileArgs &t, lds_u16 *lds) {
           if constexpr (C::FP8B) v *= ld_g16f(t.scale + n);  // per-column weight scale
           if constexpr (O == Out::F32)
             st_g16((float *)t.C + (size_t)dst_row * t.N + n, v);
-          else
+          else if constexpr (O == Out::BF16)
             st_g8_bf16((uint16_t *)t.C + (size_t)dst_row * t.N + n, v);
+          else  // H[row][n/2 .. n/2+1] from the pairs (n, n+1), (n+2, n+3)
+            st_g4_swiglu_bf16((uint16_t *)t.C + (size_t)dst_row * (t.N / 2) + n / 2, v);
         }
       }
     }

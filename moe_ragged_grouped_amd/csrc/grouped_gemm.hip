@@ -37,7 +37,7 @@ struct Params {
   const uint16_t *A;
   const uint16_t *B;
   const int32_t *off;
-  void *C;  // fp32 or bf16 [M_cap][N]
+  void *C;  // fp32 or bf16 [M_cap][N], or bf16 [M_cap][N/2] for SwiGLU
   int E, K, N, M_cap;
   int bm_fixed;  // 0 = per-expert choice
   // indexed rows (gather / scatter entry point) only
@@ -77,10 +77,13 @@ __device__ __forceinline__ void tile_body(const Params &p, int row0, int rows, i
   a.B = (const char *)uniform_ptr(B) + ((size_t)expert * K * N + col0) * Cfg::B_ELEM;
   a.scale = Cfg::FP8B ? (const float *)uniform_ptr(p.b_scale) + (size_t)expert * N + col0
                       : nullptr;
+  // bytes per C element, and C elements per product column (SwiGLU writes one
+  // bf16 per (gate, up) pair)
   constexpr size_t kOutBytes = O == Out::F32 ? 4 : 2;
+  constexpr int kColsPerOut = O == Out::SwiGluBF16 ? 2 : 1;
   if constexpr (R == Rows::Grouped) {
     a.A = (const uint16_t *)uniform_ptr(A) + (size_t)row0 * K;
-    a.C = (char *)uniform_ptr(C) + ((size_t)row0 * N + col0) * kOutBytes;
+    a.C = (char *)uniform_ptr(C) + ((size_t)row0 * N + col0) / kColsPerOut * kOutBytes;
     a.src = a.dst = nullptr;
     a.n_src = a.n_dst = 0;
   } else {
@@ -313,6 +316,14 @@ extern "C" gg_status_t gg_grouped_gemm_bf16_bf16out(const void *A, const void *B
                                                     int32_t M_cap, int32_t bm, void *stream) {
   return grouped_gemm<Out::BF16, Rows::Grouped>(
       make_params(A, B, group_offsets, C, E, K, N, M_cap, bm), stream);
+}
+
+extern "C" gg_status_t gg_grouped_gemm_bf16_swiglu(const void *A, const void *B,
+                                                   const int32_t *group_offsets, void *H,
+                                                   int32_t E, int32_t K, int32_t N, int32_t M_cap,
+                                                   int32_t bm, void *stream) {
+  return grouped_gemm<Out::SwiGluBF16, Rows::Grouped>(
+      make_params(A, B, group_offsets, H, E, K, N, M_cap, bm), stream);
 }
 
 extern "C" gg_status_t gg_grouped_gemm_bf16_gather(const void *X, int32_t n_src,

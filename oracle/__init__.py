@@ -48,6 +48,12 @@ Contents
   bf16-output product may return (the worklog's traffic model, section 2.1,
   counts C in 2-byte values).
 
+* ``silu`` / ``swiglu_pairs``: the SwiGLU activation between the gate and up
+  projections the Pearl Pulse article benchmarks ("What the 15% measures"):
+  silu(x) = x * sigmoid(x) = x / (1 + e^-x), and H[:, j] = silu(C[:, 2j]) *
+  C[:, 2j+1] for a product whose columns interleave gate (even) and up (odd)
+  -- the column layout of the fused entry point, written out directly.
+
 Every function is pinned by ``tests/test_oracle.py`` (brute force, library
 products, closed forms, the pages' printed figures); none is unpinned.
 """
@@ -341,3 +347,23 @@ def grouped_gemm_fp8w_entries(A, Bq, scale, offsets, rows, cols):
 def _bf16_to_f64(bits):
     b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
     return b.view(np.float32).astype(np.float64)
+
+
+def silu(x):
+    """silu(x) = x * sigmoid(x) = x / (1 + e^-x), in binary64.
+
+    For x below about -709, e^-x overflows to infinity and the quotient is
+    -0, while the exact value has magnitude below 1e-305.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return x / (1.0 + np.exp(-x))
+
+
+def swiglu_pairs(C):
+    """H[:, j] = silu(C[:, 2j]) * C[:, 2j+1]: gate in the even columns, up in
+    the odd ones; binary64 in and out."""
+    C = np.asarray(C, dtype=np.float64)
+    if C.shape[-1] % 2:
+        raise ValueError("an even number of columns is needed (gate, up pairs)")
+    return silu(C[..., 0::2]) * C[..., 1::2]

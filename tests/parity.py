@@ -61,3 +61,55 @@ def check_bf16(c_gpu, c_ref, s_ref, what=""):
     rel = float(np.linalg.norm(g - r)) / nr
     assert rel <= REL_FRO_BF16, "%s: relative Frobenius error %.3e" % (what, rel)
     return rel
+
+
+# SwiGLU output (gate, up column pairs) rounded to bf16. The kernel's fp32
+# gate g' and up u' meet the fp32 bar: |g' - g| <= 1e-4 * S_g, likewise u'.
+# silu falls on (-inf, x*] and rises on [x*, inf), x* = -1 - W(1/e), so over
+# an interval it is largest at an end and smallest at an end or at x*; the
+# product with the u interval is bounded by its four corners. The fp32
+# evaluation (expf within a few ulp, the sum, the IEEE division and the
+# product each within half an ulp) adds at most 2^-20 of the value, while
+# inputs stay well inside fp32's range (|g| below a few hundred), plus, where
+# e^-g overflows or the result underflows, an absolute error below
+# 2^-100 * |u| (the exact |silu(g)| is then below 3e-37). The bf16 output must
+# lie between the bf16 roundings of the widened bounds.
+SWIGLU_EVAL_REL = 2.0 ** -20
+SWIGLU_EVAL_ABS = 2.0 ** -100
+
+
+def silu_range(lo, hi):
+    """Elementwise [min, max] of silu over [lo, hi] (binary64)."""
+    import oracle
+    from scipy.special import lambertw
+    w = float(lambertw(1.0 / np.e).real)
+    x_star = -1.0 - w
+    a, b = oracle.silu(lo), oracle.silu(hi)
+    smin = np.minimum(a, b)
+    smin = np.where((lo <= x_star) & (x_star <= hi), -w, smin)
+    return smin, np.maximum(a, b)
+
+
+def swiglu_bounds(c_ref, s_ref):
+    """[lo, hi] for the fp32 SwiGLU of a product meeting the fp32 bar."""
+    c = np.asarray(c_ref, dtype=np.float64)
+    s = np.asarray(s_ref, dtype=np.float64)
+    g, u = c[..., 0::2], c[..., 1::2]
+    eg, eu = ELEM * s[..., 0::2], ELEM * s[..., 1::2]
+    sl, sh = silu_range(g - eg, g + eg)
+    corners = np.stack([sl * (u - eu), sl * (u + eu), sh * (u - eu), sh * (u + eu)])
+    lo, hi = corners.min(axis=0), corners.max(axis=0)
+    slack = SWIGLU_EVAL_REL * np.maximum(np.abs(lo), np.abs(hi)) + \
+        SWIGLU_EVAL_ABS * np.maximum(1.0, np.abs(u) + eu)
+    return lo - slack, hi + slack
+
+
+def check_swiglu_bf16(h_gpu, c_ref, s_ref, what=""):
+    import oracle
+    h = np.asarray(h_gpu, dtype=np.float64)
+    lo, hi = swiglu_bounds(c_ref, s_ref)
+    assert h.shape == lo.shape, (h.shape, lo.shape)
+    assert np.isfinite(h).all(), "%s: non-finite output" % what
+    bad = (h < oracle.round_to_bf16(lo)) | (h > oracle.round_to_bf16(hi))
+    assert not bad.any(), "%s: %d SwiGLU outputs outside their bf16 bracket (first at %s)" % (
+        what, int(bad.sum()), np.argwhere(bad)[0].tolist())

@@ -68,14 +68,17 @@ def _call(lib, fn="gg_grouped_gemm_bf16", **kw):
     (dict(E=1025), 3), (dict(M_cap=2**31 - 100), 3),
     (dict(K=2**22 + 8), 3), (dict(N=2**24 + 8), 3),
 ])
-@pytest.mark.parametrize("fn", ["gg_grouped_gemm_bf16", "gg_grouped_gemm_bf16_bf16out"])
+@pytest.mark.parametrize("fn", ["gg_grouped_gemm_bf16", "gg_grouped_gemm_bf16_bf16out",
+                                "gg_grouped_gemm_bf16_swiglu"])
 def test_host_checks(lib, kw, status, fn):
     assert _call(lib, fn, **kw) == status
 
 
-def test_empty_problem_enqueues_nothing(lib):
+@pytest.mark.parametrize("fn", ["gg_grouped_gemm_bf16", "gg_grouped_gemm_bf16_bf16out",
+                                "gg_grouped_gemm_bf16_swiglu"])
+def test_empty_problem_enqueues_nothing(lib, fn):
     # M_cap == 0: nothing to compute; returns before touching the device
-    assert _call(lib, M_cap=0) == 0
+    assert _call(lib, fn, M_cap=0) == 0
 
 
 def test_tile_schedule_host_checks(lib):

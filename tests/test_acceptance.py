@@ -1,0 +1,108 @@
+"""The GPU acceptance checks themselves, on the CPU.
+
+A float32 product computed by numpy (another summation order than the
+oracle's binary64 loop) stands in for a kernel result that meets the bar;
+each check must accept it and reject it once a plausible mistake is planted
+(a wrong sign, one element off, a transposed pairing). Nothing here runs on
+the GPU.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+from tests import parity
+
+
+def _bf16_to_f32(bits):
+    return (np.asarray(bits, dtype=np.uint32) << 16).view(np.float32)
+
+
+@pytest.fixture(scope="module")
+def case():
+    w = wl.make_workload(E=3, K=384, N=264, sizes=[40, 0, 77], seed=31)
+    ref, s, _ = oracle.grouped_gemm(w.A, w.B, w.offsets)
+    A = _bf16_to_f32(w.A)
+    B = _bf16_to_f32(w.B)
+    c32 = np.zeros((w.M_cap, w.N), dtype=np.float32)
+    for e in range(w.E):
+        r0, r1 = int(w.offsets[e]), int(w.offsets[e + 1])
+        c32[r0:r1] = A[r0:r1] @ B[e]
+    m = w.M_tot
+    return c32[:m], ref[:m], s[:m]
+
+
+def test_fp32_check_accepts_float32_product_and_rejects_mistakes(case):
+    c32, ref, s = case
+    parity.check(c32, ref, s, "float32 product")
+    with pytest.raises(AssertionError):
+        parity.check(-c32, ref, s, "sign")
+    bad = c32.copy()
+    bad[5, 17] *= 1.01
+    with pytest.raises(AssertionError):
+        parity.check(bad, ref, s, "one element")
+
+
+def test_bf16_check_accepts_rounded_product_and_rejects_mistakes(case):
+    c32, ref, s = case
+    c16 = oracle.round_to_bf16(c32.astype(np.float64))
+    parity.check_bf16(c16, ref, s, "bf16 product")
+    bad = c16.copy()
+    bad[3, 9] = oracle.round_to_bf16(bad[3, 9] * 1.02)
+    with pytest.raises(AssertionError):
+        parity.check_bf16(bad, ref, s, "one element")
+    with pytest.raises(AssertionError):
+        parity.check_bf16(c16[:, ::-1], ref, s, "columns reversed")
+
+
+def _swiglu_f32(c32):
+    g = c32[:, 0::2].astype(np.float32)
+    u = c32[:, 1::2].astype(np.float32)
+    with np.errstate(over="ignore"):
+        return (g / (np.float32(1) + np.exp(-g))) * u
+
+
+def test_swiglu_check_accepts_float32_activation_and_rejects_mistakes(case):
+    c32, ref, s = case
+    h = oracle.round_to_bf16(_swiglu_f32(c32).astype(np.float64))
+    parity.check_swiglu_bf16(h, ref, s, "float32 swiglu")
+    swapped = oracle.round_to_bf16(_swiglu_f32(c32[:, [i ^ 1 for i in range(c32.shape[1])]])
+                                   .astype(np.float64))
+    with pytest.raises(AssertionError):
+        parity.check_swiglu_bf16(swapped, ref, s, "gate and up swapped")
+    bad = h.copy()
+    bad[7, 4] = oracle.round_to_bf16(bad[7, 4] * 1.02 + 1e-3)
+    with pytest.raises(AssertionError):
+        parity.check_swiglu_bf16(bad, ref, s, "one element")
+    with pytest.raises(AssertionError):  # sigmoid instead of silu
+        g, u = c32[:, 0::2].astype(np.float64), c32[:, 1::2].astype(np.float64)
+        parity.check_swiglu_bf16(oracle.round_to_bf16(u / (1 + np.exp(-g))), ref, s, "sigmoid")
+
+
+def test_silu_range_brackets_samples():
+    rng = np.random.default_rng(4)
+    lo = rng.normal(0, 3, 2000)
+    hi = lo + rng.exponential(1.0, 2000)
+    smin, smax = parity.silu_range(lo, hi)
+    t = rng.random((2000, 64))
+    x = lo[:, None] + t * (hi - lo)[:, None]
+    v = oracle.silu(x)
+    assert (v.min(axis=1) >= smin - 1e-15).all()
+    assert (v.max(axis=1) <= smax + 1e-15).all()
+    # the interior minimum is attained: silu(x*) = -W(1/e) ~ -0.2785
+    m = (lo < -1.3) & (hi > -1.25)
+    assert m.any() and np.allclose(smin[m], -0.2784645427610738, rtol=1e-12)
+
+
+def test_swiglu_bounds_cover_saturated_gates():
+    # a gate of -200: e^200 overflows float32, the kernel returns -0 * u; the
+    # exact value is about -2.8e-85 * u; both must be inside the bracket
+    c = np.array([[-200.0, 3.0, 150.0, -2.0]])
+    s = np.array([[1.0, 1.0, 1.0, 1.0]])
+    parity.check_swiglu_bf16(np.array([[-0.0, -300.0]]), c, s, "saturated, kernel")
+    exact = oracle.swiglu_pairs(c)
+    assert -1e-80 < exact[0, 0] < 0.0
+    parity.check_swiglu_bf16(oracle.round_to_bf16(exact), c, s, "saturated, exact")
+    with pytest.raises(AssertionError):
+        parity.check_swiglu_bf16(np.array([[-1e-3, -300.0]]), c, s, "saturated, wrong")

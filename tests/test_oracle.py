@@ -450,3 +450,69 @@ def test_fp8_weight_recipe_is_close_to_bf16_weights():
     deq = oracle.decode_e4m3(q) * scale[:, None, :]
     assert (np.abs(oracle.decode_e4m3(q)).max(axis=1) == 448.0).all()
     assert (np.abs(deq - b) <= 2.0 ** -4 * np.abs(b) + 2.0 ** -10 * scale[:, None, :]).all()
+
+
+# ---- SwiGLU on (gate, up) column pairs ------------------------------------------
+
+def test_silu_against_library_sigmoid():
+    # silu(x) = x * sigmoid(x); scipy's expit is an independent sigmoid
+    special = pytest.importorskip("scipy.special")
+    x = np.concatenate([np.linspace(-60, 60, 2401), [-700.0, -30.5, -1e-12, 0.0, 1e-12, 30.5, 700.0]])
+    want = x * special.expit(x)
+    got = oracle.silu(x)
+    assert np.allclose(got, want, rtol=4e-16, atol=0.0)
+    assert oracle.silu(0.0) == 0.0
+
+
+def test_silu_closed_forms():
+    rng = np.random.default_rng(3)
+    x = rng.normal(0, 4, 10000)
+    # sigmoid(-x) = 1 - sigmoid(x), so silu(x) - silu(-x) = x
+    assert np.allclose(oracle.silu(x) - oracle.silu(-x), x, rtol=1e-14, atol=1e-14)
+    # silu(x) -> x for large x, -> 0 (from below) for very negative x
+    assert oracle.silu(40.0) == 40.0
+    assert -1e-300 < oracle.silu(-800.0) <= 0.0
+    # sigmoid(1) = e / (1 + e)
+    assert abs(oracle.silu(1.0) - math.e / (1.0 + math.e)) < 1e-16
+
+
+def test_silu_minimum_is_minus_lambert_w():
+    # silu'(x) = 0 where 1 + x + e^x = 0, i.e. x* = -1 - W(1/e); there
+    # silu(x*) = -W(1/e), the global minimum
+    special = pytest.importorskip("scipy.special")
+    w = float(special.lambertw(1.0 / math.e).real)
+    x_star = -1.0 - w
+    assert abs(oracle.silu(x_star) + w) < 1e-15
+    near = oracle.silu(np.array([x_star - 1e-4, x_star + 1e-4, -5.0, 0.0, 5.0]))
+    assert (near > -w).all()
+
+
+def test_swiglu_pairs_gate_even_up_odd():
+    special = pytest.importorskip("scipy.special")
+    C = np.array([[2.0, 3.0, -1.0, 5.0], [0.5, -4.0, 7.0, 0.25]])
+    want = np.array([[2.0 * special.expit(2.0) * 3.0, -1.0 * special.expit(-1.0) * 5.0],
+                     [0.5 * special.expit(0.5) * -4.0, 7.0 * special.expit(7.0) * 0.25]])
+    got = oracle.swiglu_pairs(C)
+    assert got.shape == (2, 2)
+    assert np.allclose(got, want, rtol=1e-15, atol=0.0)
+    # swapping gate and up changes the result (the layout is not symmetric)
+    assert not np.allclose(oracle.swiglu_pairs(C[:, [1, 0, 3, 2]]), want)
+    with pytest.raises(ValueError):
+        oracle.swiglu_pairs(np.zeros((2, 3)))
+
+
+def test_swiglu_of_identity_product_is_swiglu_of_a():
+    # B[e] = I: the product is A (exact), so H = silu(A[:, even]) * A[:, odd],
+    # computed here one scalar at a time with the math module
+    w = wl.make_workload(E=3, K=16, N=16, sizes=[3, 0, 4], seed=9)
+    B = np.zeros_like(w.B)
+    one = np.uint16(0x3F80)  # bf16 1.0
+    for e in range(3):
+        B[e][np.arange(16), np.arange(16)] = one
+    C, _, _ = oracle.grouped_gemm(w.A, B, w.offsets, want_s=False)
+    H = oracle.swiglu_pairs(C[: w.M_tot])
+    a = (w.A[: w.M_tot].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    for r in range(w.M_tot):
+        for j in range(8):
+            g, u = a[r, 2 * j], a[r, 2 * j + 1]
+            assert H[r, j] == pytest.approx(g / (1.0 + math.exp(-g)) * u, rel=1e-15, abs=0.0)

@@ -349,6 +349,90 @@ def test_bf16_out_full_size_sampled(gg):
     parity.check_bf16(out[rows, cols], c, s, "uniform16k bf16 sampled")
 
 
+# ---- SwiGLU of (gate, up) column pairs, bf16 output --------------------------------
+
+def _run_swiglu(gg, w, bm):
+    A, B, off = _dev(w)
+    H = torch.full((w.M_cap, w.N // 2), float("nan"), dtype=torch.bfloat16, device="cuda:0")
+    gg.grouped_gemm_swiglu(A, B, off, out=H, bm=bm)
+    torch.cuda.synchronize()
+    return H.float().cpu().numpy().astype(np.float64)
+
+
+def _full_compare_swiglu(gg, w, bm, what):
+    _say("case swiglu %s E=%d K=%d N=%d M_tot=%d bm=%d" % (what, w.E, w.K, w.N, w.M_tot, bm))
+    got = _run_swiglu(gg, w, bm)
+    ref, s, _ = oracle.grouped_gemm(w.A, w.B, w.offsets)
+    m = w.M_tot
+    parity.check_swiglu_bf16(got[:m], ref[:m], s[:m], what)
+    assert np.isnan(got[m:]).all(), "%s: rows past the last group were written" % what
+
+
+@pytest.mark.parametrize("bm", BMS)
+def test_swiglu_tiny(gg, bm):
+    _full_compare_swiglu(gg, wl.make_workload("tiny"), bm, "tiny")
+
+
+@pytest.mark.parametrize("bm", BMS)
+def test_swiglu_ragged_wide(gg, bm):
+    # N = 776: three full 256-wide tiles and a last one of 8 columns (4 pairs)
+    w = wl.make_workload(E=4, K=200, N=776, sizes=[300, 0, 45, 517], seed=27, M_cap=870)
+    _full_compare_swiglu(gg, w, bm, "ragged-wide")
+
+
+@pytest.mark.parametrize("bm", [0, 16, 256])
+def test_swiglu_saturating_gates(gg, bm):
+    # integer inputs in [-3, 3] with K = 512: gates spread over about +-90 and
+    # beyond, so e^-g overflows fp32 for many of them (silu -> -0) and
+    # silu(g) = g for the large positive ones
+    w = wl.make_workload(E=4, K=512, N=264, sizes=[5, 0, 130, 61], seed=23, values="int")
+    ref, _, _ = oracle.grouped_gemm(w.A, w.B, w.offsets, want_s=False)
+    g = ref[: w.M_tot, 0::2]
+    assert (g < -89).any() and (g > 20).any()
+    _full_compare_swiglu(gg, w, bm, "saturating")
+
+
+@pytest.mark.parametrize("bm", [0, 64])
+def test_swiglu_is_activated_fp32_product(gg, bm):
+    # the fused epilogue sees the same fp32 accumulators as the fp32 entry
+    # point: its output is that result's SwiGLU, within the fp32 evaluation
+    # error, rounded to bf16
+    w = wl.make_workload(E=6, K=328, N=392, sizes=[0, 1, 17, 130, 0, 300], seed=21, M_cap=470)
+    _say("case swiglu vs fp32-out bm=%d" % bm)
+    A, B, off = _dev(w)
+    c32 = gg.grouped_gemm(A, B, off, bm=bm)
+    h = gg.grouped_gemm_swiglu(A, B, off, bm=bm)
+    torch.cuda.synchronize()
+    m = w.M_tot
+    h64 = oracle.swiglu_pairs(c32[:m].cpu().numpy().astype(np.float64))
+    slack = parity.SWIGLU_EVAL_REL * np.abs(h64) + parity.SWIGLU_EVAL_ABS
+    got = h[:m].float().cpu().numpy().astype(np.float64)
+    assert (got >= oracle.round_to_bf16(h64 - slack)).all()
+    assert (got <= oracle.round_to_bf16(h64 + slack)).all()
+
+
+def test_swiglu_full_size_sampled(gg):
+    w = _full("uniform16k")
+    guard = 16
+    dev = torch.device("cuda:0")
+    A, B, off = _dev(w)
+    Hbig = torch.full((w.M_cap + guard, w.N // 2), float("nan"), dtype=torch.bfloat16, device=dev)
+    _say("case swiglu full uniform16k")
+    gg.grouped_gemm_swiglu(A, B, off, out=Hbig[: w.M_cap], bm=0)
+    torch.cuda.synchronize()
+    out = Hbig.float().cpu().numpy().astype(np.float64)
+    assert np.isfinite(out[: w.M_tot]).all()
+    assert np.isnan(out[w.M_cap:]).all()
+    rng = np.random.default_rng(9)
+    rows, cols = _samples(w, rng)
+    pairs = cols // 2
+    rr = np.repeat(rows, 2)
+    cc = np.stack([2 * pairs, 2 * pairs + 1], axis=1).ravel()
+    c, s = oracle.grouped_gemm_entries(w.A, w.B, w.offsets, rr, cc)
+    parity.check_swiglu_bf16(out[rows, pairs][:, None], c.reshape(-1, 2), s.reshape(-1, 2),
+                             "uniform16k swiglu sampled")
+
+
 # ---- rows gathered / scattered by index -------------------------------------------
 
 def _topk_routing(n_tokens, E, topk, rng):

@@ -26,7 +26,10 @@ Prints one JSON line:
 epilogue); its algorithmic bytes count C at 2 bytes per element. --out swiglu
 times the fused gate/up entry point (B's columns read as interleaved gate and
 up pairs, bf16 H of N/2 columns written); its output counts at 1 byte per
-product column.
+product column. --gather and --combine time the entry points that reach rows
+by index (a seeded top-1 permutation); --combine adds weight * row into fp32
+output rows with atomics, counted as a read and a write of every output
+element.
 """
 
 import argparse
@@ -131,6 +134,9 @@ def main():
                     help="fp8: E4M3 weights with per-column scales (a separate precision)")
     ap.add_argument("--gather", action="store_true",
                     help="time the gather/scatter entry point (A rows and C rows by index)")
+    ap.add_argument("--combine", action="store_true",
+                    help="time the gather + weighted-combine entry point (fp32 atomic adds "
+                         "into the token rows; with --gather's top-1 permutation)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (for counter calibration)")
@@ -179,6 +185,8 @@ def main():
         Bq = torch.from_numpy(q_np).to(dev)
         Bs = torch.from_numpy(sc_np).to(dev)
         del q_np
+    if args.combine:
+        args.gather = True
     if args.gather:
         # rows reached by index: X holds the routed rows in a seeded random
         # (token) order, grouped row r reads X[perm[r]] and is written back to
@@ -189,10 +197,19 @@ def main():
         X = torch.empty_like(A)
         X[torch.from_numpy(perm_np).long().to(dev)] = A
         perm = torch.from_numpy(perm_np).to(dev)
+        if args.combine:
+            # gate weights in (0, 1]; Y accumulates across steps (the kernel's
+            # work does not depend on Y's values, and clearing it inside the
+            # timed region would time a fill kernel too)
+            gate = torch.from_numpy(np.random.default_rng(w.seed + 501).uniform(
+                0.05, 1.0, w.M_cap).astype(np.float32)).to(dev)
+            C.zero_()
 
     def step():
         if args.weights == "fp8":
             gg.grouped_gemm_fp8w(A, Bq, Bs, off, out=C, bm=args.bm)
+        elif args.combine:
+            gg.grouped_gemm_gather_combine(X, perm, B, off, perm, gate, out=C, bm=args.bm)
         elif args.gather:
             gg.grouped_gemm_gather(X, perm, B, off, dst_rows=perm, out=C, bm=args.bm)
         elif args.out == "swiglu":
@@ -239,7 +256,9 @@ def main():
     active = int((w.sizes > 0).sum())
     b_bytes = 2 * w.K * w.N * active if args.weights == "bf16" else (w.K + 4) * w.N * active
     alg_bytes = (2 * w.M_tot * w.K + b_bytes + c_bytes * w.M_tot * w.N
-                 + (8 * w.M_tot if args.gather else 0))
+                 + (8 * w.M_tot if args.gather else 0)
+                 # the combine reads each Y element before adding, and reads a weight per row
+                 + (4 * w.M_tot * w.N + 4 * w.M_tot if args.combine else 0))
     intensity = useful / alg_bytes
     hbm_gbs = alg_bytes / launch_s / 1e9
     tflops_launch = useful / launch_s / 1e12
@@ -276,7 +295,8 @@ def main():
         "data": "synthetic (seeded normal draws rounded to bf16, no dataset)",
         "config": {"workload": DESCRIPTIONS[args.config], "name": args.config, "E": w.E, "K": w.K,
                    "N": w.N, "M_tot": w.M_tot, "bm": args.bm or "per-expert", "out_dtype": args.out,
-                   "rows": "gathered/scattered by index" if args.gather else "grouped",
+                   "rows": ("gathered, weighted combine by fp32 atomics" if args.combine else
+                            "gathered/scattered by index" if args.gather else "grouped"),
                    "weights": "bf16" if args.weights == "bf16"
                    else "fp8 e4m3 + fp32 scale per expert column"},
         "hbm_gbs": round(hbm_gbs, 1),

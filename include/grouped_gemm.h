@@ -158,6 +158,43 @@ gg_status_t gg_grouped_gemm_bf16_gather(const void *X, int32_t n_src, const int3
                                         int32_t M_cap, int32_t bm, void *stream);
 
 /*
+ * gg_grouped_gemm_bf16_gather_combine -- the gathered product with the
+ * weighted combine folded into the epilogue.
+ *
+ * After the expert products, each token's routed rows are weighted and
+ * summed back into the token's row (the worklog's "What I am measuring"
+ * places the permutation on either side of the grouped GEMM; the InferenceX
+ * glossary's "Engineering details" name the weighted combine). Here:
+ *   Y[dst_rows[r]][n] += row_weights[r] * C[r][n]
+ * for every grouped row r < off[E] whose destination lies in [0, n_dst),
+ * where C[r] is the product gg_grouped_gemm_bf16_gather computes for that
+ * row (A row X[src_rows[r]], weights B[e] of its expert).
+ *   X, n_src, src_rows, B, group_offsets, E, K, N, M_cap, bm, stream: as in
+ *             gg_grouped_gemm_bf16_gather.
+ *   dst_rows     int32 [M_cap] on the device, 4-byte aligned, required.
+ *                Several grouped rows may name the same Y row (top-k).
+ *   row_weights  fp32 [M_cap] on the device, 4-byte aligned, required.
+ *   Y            fp32 [n_dst][N], row-major, 16-byte aligned, in device
+ *                memory (hipMalloc; the adds are the GPU's fp32 atomics):
+ *                accumulated into, not overwritten -- clear it first for a
+ *                plain combine. Rows no grouped row names keep their values.
+ *   n_dst >= 0.
+ * Each term is the fp32 product row times its weight, rounded once; the
+ * terms meeting in one element are added with fp32 atomic adds in an
+ * unspecified order, so the result may differ between runs by the rounding
+ * of that order (the product itself is as accurate as gg_grouped_gemm_bf16).
+ * Status codes as for gg_grouped_gemm_bf16_gather; a null dst_rows or
+ * row_weights, or n_dst < 0, is GG_ERR_INVALID_VALUE.
+ */
+gg_status_t gg_grouped_gemm_bf16_gather_combine(const void *X, int32_t n_src,
+                                                const int32_t *src_rows, const void *B,
+                                                const int32_t *group_offsets,
+                                                const int32_t *dst_rows,
+                                                const float *row_weights, float *Y, int32_t n_dst,
+                                                int32_t E, int32_t K, int32_t N, int32_t M_cap,
+                                                int32_t bm, void *stream);
+
+/*
  * gg_grouped_gemm_fp8w -- the product with fp8 weights and per-column scales
  * (the Pearl Pulse article, "What the 15% measures", notes that its kernel
  * ships with an FP8 scheme; the scheme below is this library's reading).

@@ -14,7 +14,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["grouped_gemm", "grouped_gemm_swiglu", "grouped_gemm_gather", "grouped_gemm_fp8w", "tile_schedule", "library_path", "load_library", "GroupedGemmError",
+__all__ = ["grouped_gemm", "grouped_gemm_swiglu", "grouped_gemm_gather", "grouped_gemm_gather_combine", "grouped_gemm_fp8w", "tile_schedule", "library_path", "load_library", "GroupedGemmError",
            "BM_CHOICES", "TILE_N", "TILE_WIDTH", "MAX_EXPERTS", "SYMBOLS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -25,8 +25,8 @@ TILE_N = 256                      # tile width (every height)
 TILE_WIDTH = {h: TILE_N for h in BM_CHOICES}  # per tile height
 MAX_EXPERTS = 1024
 SYMBOLS = ("gg_grouped_gemm_bf16", "gg_grouped_gemm_bf16_bf16out", "gg_grouped_gemm_bf16_swiglu",
-           "gg_grouped_gemm_bf16_gather", "gg_grouped_gemm_fp8w", "gg_tile_schedule",
-           "gg_status_string")
+           "gg_grouped_gemm_bf16_gather", "gg_grouped_gemm_bf16_gather_combine",
+           "gg_grouped_gemm_fp8w", "gg_tile_schedule", "gg_status_string")
 
 _lib = None
 
@@ -57,6 +57,9 @@ def load_library():
         lib.gg_grouped_gemm_bf16_gather.argtypes = [vp, i32, vp, vp, vp, vp, vp, i32, i32, i32, i32,
                                                     i32, vp]
         lib.gg_grouped_gemm_bf16_gather.restype = ctypes.c_int
+        lib.gg_grouped_gemm_bf16_gather_combine.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, i32,
+                                                            i32, i32, i32, i32, i32, vp]
+        lib.gg_grouped_gemm_bf16_gather_combine.restype = ctypes.c_int
         lib.gg_grouped_gemm_fp8w.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
         lib.gg_grouped_gemm_fp8w.restype = ctypes.c_int
         lib.gg_tile_schedule.argtypes = [vp, i32, i32, i32, i32, vp, vp, i32, vp]
@@ -191,6 +194,51 @@ def grouped_gemm_gather(X, src_rows, B, offsets, dst_rows=None, out=None, bm: in
         dst_rows.data_ptr() if dst_rows is not None else None, E, K, N, M_cap, int(bm),
         _stream_handle(X.device, stream))
     _check(st, "gg_grouped_gemm_bf16_gather")
+    return out
+
+
+def grouped_gemm_gather_combine(X, src_rows, B, offsets, dst_rows, weights, out=None,
+                                n_dst=None, bm: int = 0, stream=None):
+    """out[dst_rows[r]] += weights[r] * (X[src_rows[r]] @ B[e(r)]) for every routed row r, in one launch.
+
+    X, src_rows, B, offsets, bm, stream as in grouped_gemm_gather; dst_rows
+    int32 [M_cap] and weights fp32 [M_cap] (device) are required. out: fp32
+    [n_dst, N], accumulated into (default: zeros with n_dst = n_src rows, the
+    token rows). Destinations outside [0, n_dst) are skipped. The adds are
+    fp32 atomics, so the rounding of each element's sum depends on the order
+    the adds land in.
+    """
+    import torch
+    lib = load_library()
+    if X.dtype != torch.bfloat16 or B.dtype != torch.bfloat16:
+        raise TypeError("X and B must be bfloat16")
+    if (src_rows.dtype != torch.int32 or offsets.dtype != torch.int32
+            or dst_rows.dtype != torch.int32):
+        raise TypeError("src_rows, dst_rows and offsets must be int32")
+    if weights.dtype != torch.float32:
+        raise TypeError("weights must be float32")
+    if (X.dim() != 2 or B.dim() != 3 or offsets.dim() != 1 or src_rows.dim() != 1
+            or dst_rows.dim() != 1 or weights.dim() != 1):
+        raise ValueError("shapes: X [n_src,K], src_rows/dst_rows/weights [M_cap], B [E,K,N], "
+                         "offsets [E+1]")
+    tensors = [X, B, offsets, src_rows, dst_rows, weights]
+    if not all(t.is_cuda and t.is_contiguous() for t in tensors):
+        raise ValueError("all tensors must be contiguous device tensors")
+    E, K, N = B.shape
+    n_src, M_cap = X.shape[0], src_rows.shape[0]
+    if (X.shape[1] != K or offsets.shape[0] != E + 1 or dst_rows.shape[0] != M_cap
+            or weights.shape[0] != M_cap):
+        raise ValueError("shape mismatch")
+    if out is None:
+        out = torch.zeros((n_src if n_dst is None else int(n_dst), N), dtype=torch.float32,
+                          device=X.device)
+    elif out.dtype != torch.float32 or out.dim() != 2 or out.shape[1] != N or not out.is_contiguous():
+        raise ValueError("out must be a contiguous fp32 [n_dst, N] tensor")
+    st = lib.gg_grouped_gemm_bf16_gather_combine(
+        X.data_ptr(), n_src, src_rows.data_ptr(), B.data_ptr(), offsets.data_ptr(),
+        dst_rows.data_ptr(), weights.data_ptr(), out.data_ptr(), out.shape[0], E, K, N, M_cap,
+        int(bm), _stream_handle(X.device, stream))
+    _check(st, "gg_grouped_gemm_bf16_gather_combine")
     return out
 
 

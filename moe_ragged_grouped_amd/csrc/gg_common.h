@@ -20,6 +20,8 @@ typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) uint16_t lds_u16;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) float lds_f32;
+typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
 
 constexpr int kThreads = 512;  // eight 64-lane waves per workgroup
 constexpr int kWave = 64;
@@ -76,6 +78,10 @@ __device__ __forceinline__ u32x4 ld_buf16(buf_rsrc r, uint32_t voff, uint32_t so
 typedef __attribute__((address_space(1))) const int32_t gbl_ci32;
 __device__ __forceinline__ int ld_g4(const int32_t *p) { return *(gbl_ci32 *)p; }
 
+// One 4-byte global load of a float (global_load_dword).
+typedef __attribute__((address_space(1))) const float gbl_cf32;
+__device__ __forceinline__ float ld_g4f(const float *p) { return *(gbl_cf32 *)p; }
+
 // One 16-byte global load of four floats (global_load_dwordx4).
 typedef __attribute__((address_space(1))) const f32x4 gbl_cf32x4;
 __device__ __forceinline__ f32x4 ld_g16f(const float *p) { return *(gbl_cf32x4 *)p; }
@@ -99,9 +105,10 @@ __device__ __forceinline__ void fp8x16_to_bf16x16(u32x4 in, u32x4 &lo, u32x4 &hi
 // One 16-byte global store (global_store_dwordx4).
 __device__ __forceinline__ void st_g16(float *p, f32x4 v) { *(gbl_f32x4 *)p = v; }
 
-// What the epilogue writes: C in fp32, C rounded to bf16, or the SwiGLU of
-// interleaved (gate, up) column pairs rounded to bf16 (half as many columns).
-enum class Out { F32, BF16, SwiGluBF16 };
+// What the epilogue writes: C in fp32, C rounded to bf16, the SwiGLU of
+// interleaved (gate, up) column pairs rounded to bf16 (half as many columns),
+// or (AddF32) each row times its weight added into fp32 destination rows.
+enum class Out { F32, BF16, SwiGluBF16, AddF32 };
 
 typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
 typedef __attribute__((address_space(1))) bf16x4 gbl_bf16x4;
@@ -123,6 +130,14 @@ __device__ __forceinline__ float silu(float x) { return x / (1.0f + expf(-x)); }
 __device__ __forceinline__ void st_g4_swiglu_bf16(uint16_t *p, f32x4 v) {
   const f32x2 h = {silu(v.x) * v.y, silu(v.z) * v.w};
   *(gbl_bf16x2 *)p = __builtin_convertvector(h, bf16x2);
+}
+
+// *p += v: one fp32 atomic add (global_atomic_add_f32, no return value;
+// device memory). Adds to one element from several lanes or workgroups land
+// in an unspecified order, each rounded once.
+typedef __attribute__((address_space(1))) float gbl_f32;
+__device__ __forceinline__ void atomic_add(float *p, float v) {
+  __builtin_amdgcn_global_atomic_fadd_f32((gbl_f32 *)p, v);
 }
 
 // Transposing LDS read of a 4 (rows) x 16 (16-bit columns) block per 16-lane

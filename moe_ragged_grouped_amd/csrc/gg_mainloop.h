@@ -106,6 +106,7 @@ struct TileArgs {
   const int32_t *dst;  // dst_rows + row0, or null
   int n_src;           // rows of X; a source index outside [0, n_src) reads zeros
   int n_dst;           // rows of C; a destination outside [0, n_dst) is not written
+  const float *wts;    // combine only: row_weights + row0 (grouped row r adds wts[r] * C)
 };
 
 // Register staging: the A chunks of the next AD K slices (slice s in
@@ -262,11 +263,76 @@ __device__ __forceinline__ void mma_stage(f32x4 (&acc)[C::NI][C::MI], const lds_
   }
 }
 
+// The wave's LDS accesses issued so far have completed (so its other lanes
+// see its writes), and the compiler moves no memory access across this
+// point. A wave's LDS region shared by no other wave needs nothing more.
+__device__ __forceinline__ void wave_lds_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// Epilogue of the weighted combine: Y[dst[r]][n] += w[r] * C[r][n].
+//
+// The accumulator layout gives each lane four adjacent columns of one row,
+// so one atomic instruction straight from it would touch 16 rows, 4 values
+// of each. The atomic units of the L2 serve requests far faster when a
+// wave's 64 lanes hit consecutive addresses (about 4x, measured with plain
+// atomic kernels). So each wave stages one 16-row slab of its block at a
+// time in LDS (already weighted) and reads it back row-major: every atomic
+// instruction then covers 64 consecutive floats, one row of a 64-wide wave
+// block or two rows of a 32-wide one. A wave uses only its own LDS region;
+// a workgroup barrier at the end keeps the next tile's first LDS stores
+// from overwriting a region another wave is still reading.
+template <class C>
+__device__ __forceinline__ void combine_epilogue(const TileArgs &t, f32x4 (&acc)[C::NI][C::MI],
+                                                 lds_f32 *lds, int wave, int lane, int wm0,
+                                                 int wn0) {
+  constexpr int P = C::WTN + 4;         // row pitch of a staged slab (floats)
+  constexpr int RPI = kWave / C::WTN;   // slab rows per atomic instruction
+  static_assert(C::WTN * RPI == kWave && 16 % RPI == 0, "a row (or two) per instruction");
+  static_assert(kThreads / kWave * 16 * P * 4 <= C::LDS_BYTES, "staging fits the stages");
+  lds_f32 *const stage = lds + wave * 16 * P;
+  const int g = lane / 16, s = lane % 16;
+  const int rr = lane / C::WTN, cc = lane % C::WTN;  // read-back position in a row group
+  const bool col_ok = wn0 + cc < t.ncols;
+#pragma unroll
+  for (int mi = 0; mi < C::MI; ++mi) {
+    // lane s (and s + 16, s + 32, s + 48) owns slab row s: its destination
+    // (-1 when there is none) and weight
+    const int m = wm0 + mi * 16 + s;
+    int d = -1;
+    float w = 0.0f;
+    if (m < t.rows) {
+      const int x = ld_g4(t.dst + m);
+      if (x >= 0 && x < t.n_dst) {
+        d = x;
+        w = ld_g4f(t.wts + m);
+      }
+    }
+#pragma unroll
+    for (int ni = 0; ni < C::NI; ++ni)
+      *(lds_f32x4 *)(stage + s * P + ni * 16 + 4 * g) = acc[ni][mi] * w;
+    // the wave's own LDS writes are complete before it reads them back
+    wave_lds_fence();
+    float v[16 / RPI];
+#pragma unroll
+    for (int k = 0; k < 16; k += RPI) v[k / RPI] = stage[(k + rr) * P + cc];
+    // the reads are complete before the next slab overwrites the region
+    wave_lds_fence();
+#pragma unroll
+    for (int k = 0; k < 16; k += RPI) {
+      // destination of slab row k + rr, held by lane k + rr
+      const int d0 = __builtin_amdgcn_readlane(d, k);
+      const int dr = RPI == 1 ? d0 : (rr == 0 ? d0 : __builtin_amdgcn_readlane(d, k + 1));
+      if (dr >= 0 && col_ok) atomic_add((float *)t.C + (size_t)dr * t.N + wn0 + cc, v[k / RPI]);
+    }
+  }
+  __syncthreads();
+}
+
 // Full K loop and epilogue for one tile. lds must hold C::LDS_BYTES. Ends with
 // a workgroup barrier, so the next tile may refill the stages at once. O is
 // what the epilogue writes: fp32 C (the accumulators as they are), bf16 C
-// (rounded to nearest even), or bf16 SwiGLU of (gate, up) column pairs into
-// an output N/2 columns wide. R says where rows come from and go.
+// (rounded to nearest even), bf16 SwiGLU of (gate, up) column pairs into an
+// output N/2 columns wide, or (indexed rows only) weight * C added into the
+// destination rows with fp32 atomics. R says where rows come from and go.
 template <class C, Out O, Rows R>
 __device__ __forceinline__ void run_tile(const TileArgs &t, lds_u16 *lds) {
   lds_u16 *const As0 = lds;                       // stage s: As0 + s * A_STAGE
@@ -336,6 +402,10 @@ __device__ __forceinline__ void run_tile(const TileArgs &t, lds_u16 *lds) {
 
   // epilogue: lane holds C[m][n..n+3] for m = s, n = 4g within each 16x16 block
   const int g = lane / 16, s = lane % 16;
+  if constexpr (O == Out::AddF32) {
+    combine_epilogue<C>(t, acc, (lds_f32 *)lds, wave, lane, wm0, wn0);
+    return;
+  }
 #pragma unroll
   for (int mi = 0; mi < C::MI; ++mi) {
     const int m = wm0 + mi * 16 + s;
@@ -357,7 +427,7 @@ __device__ __forceinline__ void run_tile(const TileArgs &t, lds_u16 *lds) {
             st_g16((float *)t.C + (size_t)dst_row * t.N + n, v);
           else if constexpr (O == Out::BF16)
             st_g8_bf16((uint16_t *)t.C + (size_t)dst_row * t.N + n, v);
-          else  // H[row][n/2 .. n/2+1] from the pairs (n, n+1), (n+2, n+3)
+          else  // H[row][n/2, n/2+1] from pairs (n, n+1), (n+2, n+3)
             st_g4_swiglu_bf16((uint16_t *)t.C + (size_t)dst_row * (t.N / 2) + n / 2, v);
         }
       }

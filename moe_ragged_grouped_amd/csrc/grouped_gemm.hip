@@ -45,6 +45,8 @@ struct Params {
   const int32_t *dst_rows;  // [M_cap] or null: grouped row r writes C row dst_rows[r]
   int n_src;                // rows of A in the indexed form
   const float *b_scale;     // fp8 weights only: [E][N] per-column scales
+  int n_dst;                // indexed form: rows of C (M_cap, or the combine's n_dst)
+  const float *row_w;       // combine only: [M_cap] weight of each grouped row
 };
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
@@ -79,7 +81,7 @@ __device__ __forceinline__ void tile_body(const Params &p, int row0, int rows, i
                       : nullptr;
   // bytes per C element, and C elements per product column (SwiGLU writes one
   // bf16 per (gate, up) pair)
-  constexpr size_t kOutBytes = O == Out::F32 ? 4 : 2;
+  constexpr size_t kOutBytes = (O == Out::F32 || O == Out::AddF32) ? 4 : 2;
   constexpr int kColsPerOut = O == Out::SwiGluBF16 ? 2 : 1;
   if constexpr (R == Rows::Grouped) {
     a.A = (const uint16_t *)uniform_ptr(A) + (size_t)row0 * K;
@@ -93,8 +95,9 @@ __device__ __forceinline__ void tile_body(const Params &p, int row0, int rows, i
     a.dst = dst ? dst + row0 : nullptr;
     a.C = (char *)uniform_ptr(C) + ((size_t)(dst ? 0 : row0) * N + col0) * kOutBytes;
     a.n_src = uniform(p.n_src);
-    a.n_dst = uniform(p.M_cap);
+    a.n_dst = uniform(p.n_dst);
   }
+  a.wts = O == Out::AddF32 ? (const float *)uniform_ptr(p.row_w) + row0 : nullptr;
   a.rows = uniform(rows);
   a.K = K;
   a.N = N;
@@ -276,6 +279,11 @@ static gg_status_t grouped_gemm(Params p, void *stream) {
     // the A resource covers all of X with 32-bit offsets
     if ((long long)p.n_src * p.K * 2 > (1LL << 31)) return GG_ERR_UNSUPPORTED;
   }
+  if constexpr (O == Out::AddF32) {
+    static_assert(R == Rows::Indexed, "the combine scatters by index");
+    if (p.dst_rows == nullptr || p.row_w == nullptr || p.n_dst < 0) return GG_ERR_INVALID_VALUE;
+    if (!aligned(p.row_w, 4)) return GG_ERR_MISALIGNED;
+  }
   if constexpr (F8) {
     if (p.b_scale == nullptr) return GG_ERR_INVALID_VALUE;
     if (!aligned(p.b_scale, 16)) return GG_ERR_MISALIGNED;
@@ -295,7 +303,7 @@ static gg_status_t grouped_gemm(Params p, void *stream) {
 static Params make_params(const void *A, const void *B, const int32_t *off, void *C, int32_t E,
                           int32_t K, int32_t N, int32_t M_cap, int32_t bm) {
   return Params{static_cast<const uint16_t *>(A), static_cast<const uint16_t *>(B), off, C, E, K,
-                N, M_cap, bm, nullptr, nullptr, 0, nullptr};
+                N, M_cap, bm, nullptr, nullptr, 0, nullptr, M_cap, nullptr};
 }
 
 }  // namespace gg
@@ -337,6 +345,19 @@ extern "C" gg_status_t gg_grouped_gemm_bf16_gather(const void *X, int32_t n_src,
   p.dst_rows = dst_rows;
   p.n_src = n_src;
   return grouped_gemm<Out::F32, Rows::Indexed>(p, stream);
+}
+
+extern "C" gg_status_t gg_grouped_gemm_bf16_gather_combine(
+    const void *X, int32_t n_src, const int32_t *src_rows, const void *B,
+    const int32_t *group_offsets, const int32_t *dst_rows, const float *row_weights, float *Y,
+    int32_t n_dst, int32_t E, int32_t K, int32_t N, int32_t M_cap, int32_t bm, void *stream) {
+  Params p = make_params(X, B, group_offsets, Y, E, K, N, M_cap, bm);
+  p.src_rows = src_rows;
+  p.dst_rows = dst_rows;
+  p.n_src = n_src;
+  p.n_dst = n_dst;
+  p.row_w = row_weights;
+  return grouped_gemm<Out::AddF32, Rows::Indexed>(p, stream);
 }
 
 extern "C" gg_status_t gg_grouped_gemm_fp8w(const void *A, const void *Bq, const float *b_scale,

@@ -48,6 +48,15 @@ Contents
   bf16-output product may return (the worklog's traffic model, section 2.1,
   counts C in 2-byte values).
 
+* ``grouped_gemm_combine``: the weighted combine after the grouped product:
+  Y[dst[r]] += w[r] * C_grouped[r] for every routed row r whose destination
+  is in range, starting from Y0 (zeros by default), in binary64. The
+  permutation and combine are the steps either side of the measured GEMM in
+  the worklog's "What I am measuring"; the InferenceX glossary's
+  "Engineering details" name the weighted combine after the expert
+  products. Also returns, per element, sum_r |w[r]| * S[r] (the product's
+  error budget carried through the weights), |Y0| + sum_r |w[r] * C[r]| and
+  the number of terms.
 * ``silu`` / ``swiglu_pairs``: the SwiGLU activation between the gate and up
   projections the Pearl Pulse article benchmarks ("What the 15% measures"):
   silu(x) = x * sigmoid(x) = x / (1 + e^-x), and H[:, j] = silu(C[:, 2j]) *
@@ -367,3 +376,34 @@ def swiglu_pairs(C):
     if C.shape[-1] % 2:
         raise ValueError("an even number of columns is needed (gate, up pairs)")
     return silu(C[..., 0::2]) * C[..., 1::2]
+
+
+def grouped_gemm_combine(X, src_rows, B, offsets, dst_rows, weights, n_dst, Y0=None):
+    """Gather, grouped product, weighted scatter-add (binary64).
+
+    X: bf16 bits [n_src, K]; src_rows, dst_rows: int [M_cap]; weights: float
+    [M_cap]; B: bf16 bits [E, K, N]; offsets: [E+1]; Y0: optional [n_dst, N]
+    starting values. Returns (Y, SW, AY, terms): Y[d] = Y0[d] + sum of
+    weights[r] * C[r] over routed rows r < off[E] with dst_rows[r] = d;
+    SW[d] = sum |weights[r]| * S[r]; AY[d] = |Y0[d]| + sum |weights[r] * C[r]|;
+    terms[d] = the number of additions into row d (Y0 counts as one).
+    """
+    off = np.asarray(offsets, dtype=np.int64)
+    m_tot = int(off[-1])
+    src = np.asarray(src_rows, dtype=np.int64)
+    dst = np.asarray(dst_rows, dtype=np.int64)
+    w = np.asarray(weights, dtype=np.float64)
+    N = B.shape[2]
+    Cg, Sg = grouped_gemm_indexed(X, src, B, off, dst_rows=None, M_cap=max(m_tot, 1))
+    Y = np.zeros((n_dst, N)) if Y0 is None else np.array(Y0, dtype=np.float64)
+    AY = np.abs(Y)
+    SW = np.zeros((n_dst, N))
+    terms = np.zeros(n_dst, dtype=np.int64) if Y0 is None else np.ones(n_dst, dtype=np.int64)
+    for r in range(m_tot):
+        d = int(dst[r])
+        if 0 <= d < n_dst:
+            Y[d] += w[r] * Cg[r]
+            SW[d] += abs(w[r]) * Sg[r]
+            AY[d] += np.abs(w[r] * Cg[r])
+            terms[d] += 1
+    return Y, SW, AY, terms

@@ -113,3 +113,23 @@ def check_swiglu_bf16(h_gpu, c_ref, s_ref, what=""):
     bad = (h < oracle.round_to_bf16(lo)) | (h > oracle.round_to_bf16(hi))
     assert not bad.any(), "%s: %d SwiGLU outputs outside their bf16 bracket (first at %s)" % (
         what, int(bad.sum()), np.argwhere(bad)[0].tolist())
+
+
+# Weighted combine Y[d] = Y0[d] + sum_r w_r * C_r with fp32 atomics. Each
+# term w_r * C'_r (C' meeting the fp32 bar) is off by at most
+# |w_r| * 1e-4 * S_r plus one fp32 rounding; the additions into one element,
+# in whatever order they land, add at most (terms - 1) roundings of the
+# running sums (each below sum |terms|). The bound used:
+# |Y_gpu - Y_ref| <= 1e-4 * sum_r |w_r| S_r + (terms + 1) * 2^-23 * (|Y0| + sum_r |w_r C_r|),
+# i.e. twice the unit roundoff per operation, which also covers the
+# difference between |C'| and |C| in the second sum.
+def check_combine(y_gpu, y_ref, sw, ay, terms, what=""):
+    y = np.asarray(y_gpu, dtype=np.float64)
+    r = np.asarray(y_ref, dtype=np.float64)
+    assert y.shape == r.shape, (y.shape, r.shape)
+    assert np.isfinite(y).all(), "%s: non-finite output" % what
+    bound = ELEM * np.asarray(sw) + (np.asarray(terms)[:, None] + 1) * 2.0 ** -23 * np.asarray(ay)
+    d = np.abs(y - r)
+    bad = d > bound
+    assert not bad.any(), "%s: %d combined elements beyond the bound (worst ratio %.3e)" % (
+        what, int(bad.sum()), float(np.max(d / np.maximum(bound, 1e-300))))

@@ -108,3 +108,28 @@ def test_gather_host_checks(lib):
     assert call(dst=70) == 2
     assert call(n_src=2 ** 22 + 1) == 3        # n_src * K * 2 > 2^31
     assert call(M_cap=0) == 0                  # nothing to do
+
+
+def test_gather_combine_host_checks(lib):
+    f = lib.gg_grouped_gemm_bf16_gather_combine
+    names = ["X", "n_src", "src", "B", "off", "dst", "w", "Y", "n_dst", "E", "K", "N", "M_cap",
+             "bm"]
+    ok = [16, 10, 64, 32, 64, 96, 48, 128, 10, 4, 256, 256, 29, 0]
+
+    def call(**kw):
+        a = list(ok)
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return f(*a, None)
+    assert call(dst=0) == 1                    # the combine needs destinations
+    assert call(w=0) == 1                      # and weights
+    assert call(n_dst=-1) == 1
+    assert call(Y=0) == 1
+    assert call(src=0) == 1
+    assert call(w=50) == 2                     # misaligned weights
+    assert call(Y=136) == 2                    # misaligned Y
+    assert call(dst=98) == 2
+    assert call(N=100) == 2
+    assert call(bm=48) == 1
+    assert call(n_src=2 ** 22 + 1) == 3
+    assert call(M_cap=0) == 0                  # nothing to do

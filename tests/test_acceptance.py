@@ -106,3 +106,32 @@ def test_swiglu_bounds_cover_saturated_gates():
     parity.check_swiglu_bf16(oracle.round_to_bf16(exact), c, s, "saturated, exact")
     with pytest.raises(AssertionError):
         parity.check_swiglu_bf16(np.array([[-1e-3, -300.0]]), c, s, "saturated, wrong")
+
+
+def test_combine_check_accepts_float32_atomics_and_rejects_mistakes():
+    rng = np.random.default_rng(15)
+    n_tokens, E, K, N, topk = 40, 6, 256, 40, 3
+    pairs = sorted((int(e), t) for t in range(n_tokens) for e in rng.choice(E, topk, replace=False))
+    sizes = np.bincount([p[0] for p in pairs], minlength=E)
+    src = np.array([p[1] for p in pairs], dtype=np.int32)
+    w = wl.make_workload(E=E, K=K, N=N, sizes=[int(x) for x in sizes], seed=16)
+    X = wl.make_workload(E=1, K=K, N=8, sizes=[n_tokens], seed=17).A
+    gate = rng.random(len(src)).astype(np.float32)
+    Y, SW, AY, terms = oracle.grouped_gemm_combine(X, src, w.B, w.offsets, src, gate, n_tokens)
+    # float32 stand-in: float32 products, weights applied in float32, terms
+    # added in a shuffled order in float32
+    xf, bf = _bf16_to_f32(X), _bf16_to_f32(w.B)
+    experts = np.repeat(np.arange(E), sizes)
+    y32 = np.zeros((n_tokens, N), dtype=np.float32)
+    for r in rng.permutation(len(src)):
+        y32[src[r]] += gate[r] * (xf[src[r]] @ bf[experts[r]])
+    parity.check_combine(y32, Y, SW, AY, terms, "float32 combine")
+    with pytest.raises(AssertionError):  # a route dropped
+        y_bad = y32.copy()
+        y_bad[src[0]] -= gate[0] * (xf[src[0]] @ bf[experts[0]])
+        parity.check_combine(y_bad, Y, SW, AY, terms, "dropped route")
+    with pytest.raises(AssertionError):  # weights ignored
+        y_bad = np.zeros_like(y32)
+        for r in range(len(src)):
+            y_bad[src[r]] += xf[src[r]] @ bf[experts[r]]
+        parity.check_combine(y_bad, Y, SW, AY, terms, "unweighted")

@@ -47,7 +47,7 @@ def test_no_spills_no_scratch(resources):
     # five single heights + the per-expert mix, each for fp32 C, bf16 C,
     # bf16 SwiGLU output, fp32 C with gathered / scattered rows, and fp8
     # weights
-    assert len(gemm) == 30, sorted(resources)
+    assert len(gemm) == 36, sorted(resources)
     for name, r in resources.items():
         assert r.get("VGPRs Spill", 0) == 0, (name, r)
         assert r.get("SGPRs Spill", 0) == 0, (name, r)

@@ -516,3 +516,69 @@ def test_swiglu_of_identity_product_is_swiglu_of_a():
         for j in range(8):
             g, u = a[r, 2 * j], a[r, 2 * j + 1]
             assert H[r, j] == pytest.approx(g / (1.0 + math.exp(-g)) * u, rel=1e-15, abs=0.0)
+
+
+# ---- weighted combine after the grouped product ----------------------------------
+
+def _routing(n_tokens, E, topk, rng):
+    pairs = sorted((int(e), t, k) for t in range(n_tokens)
+                   for k, e in enumerate(rng.choice(E, size=topk, replace=False)))
+    sizes = np.bincount([p[0] for p in pairs], minlength=E)
+    src = np.array([p[1] for p in pairs], dtype=np.int32)
+    slot = np.array([p[2] for p in pairs], dtype=np.int32)
+    expert = np.array([p[0] for p in pairs], dtype=np.int32)
+    return sizes, src, slot, expert
+
+
+def test_combine_brute_force_token_major():
+    # Y[t] = sum over token t's routes (e, w) of w * (x_t @ B[e]), computed
+    # token by token with scalar Python loops, independent of the grouped
+    # layout the oracle works in
+    rng = np.random.default_rng(12)
+    n_tokens, E, K, N, topk = 7, 4, 6, 5, 2
+    sizes, src, slot, expert = _routing(n_tokens, E, topk, rng)
+    w = wl.make_workload(E=E, K=K, N=N, sizes=[int(x) for x in sizes], seed=5, values="int")
+    X = wl.make_workload(E=1, K=K, N=8, sizes=[n_tokens], seed=6, values="int").A
+    gate = rng.choice([0.25, 0.5, 0.75, 1.0, -0.5], size=len(src))
+    Y, _, _, terms = oracle.grouped_gemm_combine(X, src, w.B, w.offsets, src, gate, n_tokens)
+    xf = (X.astype(np.uint32) << 16).view(np.float32)
+    bf = (w.B.astype(np.uint32) << 16).view(np.float32)
+    for t in range(n_tokens):
+        for n in range(N):
+            want = 0.0
+            for r in range(len(src)):
+                if src[r] == t:
+                    want += gate[r] * sum(float(xf[t, k]) * float(bf[expert[r], k, n]) for k in range(K))
+            assert Y[t, n] == want
+    assert (terms == topk).all()
+
+
+def test_combine_top1_unit_weight_is_the_scatter():
+    rng = np.random.default_rng(13)
+    sizes, src, _, _ = _routing(20, 5, 1, rng)
+    w = wl.make_workload(E=5, K=40, N=24, sizes=[int(x) for x in sizes], seed=7)
+    X = wl.make_workload(E=1, K=40, N=8, sizes=[20], seed=8).A
+    Y, SW, _, _ = oracle.grouped_gemm_combine(X, src, w.B, w.offsets, src, np.ones(len(src)), 20)
+    C, S = oracle.grouped_gemm_indexed(X, src, w.B, w.offsets, dst_rows=src, M_cap=20)
+    assert np.array_equal(Y, C) and np.array_equal(SW, S)
+
+
+def test_combine_linear_in_weights_and_start_values():
+    rng = np.random.default_rng(14)
+    sizes, src, _, _ = _routing(16, 6, 3, rng)
+    w = wl.make_workload(E=6, K=32, N=16, sizes=[int(x) for x in sizes], seed=9)
+    X = wl.make_workload(E=1, K=32, N=8, sizes=[16], seed=10).A
+    g = rng.random(len(src))
+    Y1, _, _, _ = oracle.grouped_gemm_combine(X, src, w.B, w.offsets, src, g, 16)
+    Y2, _, _, _ = oracle.grouped_gemm_combine(X, src, w.B, w.offsets, src, 2.0 * g, 16)
+    assert np.array_equal(Y2, 2.0 * Y1)  # scaling by 2 is exact
+    Y0 = rng.normal(size=(16, 16))
+    Y3, _, AY, terms = oracle.grouped_gemm_combine(X, src, w.B, w.offsets, src, g, 16, Y0=Y0)
+    assert np.allclose(Y3, Y0 + Y1, rtol=1e-13, atol=1e-13)
+    assert (terms == 4).all() and (AY >= np.abs(Y0)).all()
+    # destinations out of range are dropped; a negative weight subtracts
+    dst = src.copy()
+    dst[0] = 16
+    Y4, _, _, _ = oracle.grouped_gemm_combine(X, src, w.B, w.offsets, dst, g, 16)
+    C, _ = oracle.grouped_gemm_indexed(X, src, w.B, w.offsets, dst_rows=None, M_cap=len(src))
+    assert np.allclose(Y4[src[0]], Y1[src[0]] - g[0] * C[0], rtol=1e-12, atol=1e-12)

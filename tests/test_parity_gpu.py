@@ -564,6 +564,97 @@ def test_gather_decode_shape_sampled(gg):
     assert (d <= parity.ELEM * s).all()
 
 
+# ---- weighted combine folded into the epilogue ----------------------------------------
+
+def _combine_case(gg, n_tokens, E, K, N, topk, seed, bm, values="normal", weights=None,
+                  y0=False, pad=0, drop=0):
+    rng = np.random.default_rng(seed)
+    sizes, src, dst_slot = _topk_routing(n_tokens, E, topk, rng)
+    dst = (dst_slot // topk).astype(np.int32)  # the token row
+    if drop:
+        dst[rng.choice(len(dst), size=drop, replace=False)] = n_tokens + 5  # out of range
+    w = wl.make_workload(E=E, K=K, N=N, sizes=[int(x) for x in sizes], seed=seed,
+                         M_cap=int(sizes.sum()) + pad, values=values)
+    X = wl.make_workload(E=1, K=K, N=8, sizes=[n_tokens], seed=seed + 1000, values=values).A
+    if weights is None:  # per-token gate weights summing to 1, as after a softmax
+        wt = rng.dirichlet(np.ones(topk), size=n_tokens)
+        g = wt[dst_slot // topk, dst_slot % topk]
+    else:
+        g = weights(rng, len(src))
+    g = np.asarray(g, dtype=np.float32)
+    M_cap = w.M_cap
+    src_full = np.concatenate([src, np.full(pad, -1, np.int32)])
+    dst_full = np.concatenate([dst, np.full(pad, 0, np.int32)])  # padding rows never run
+    g_full = np.concatenate([g, np.full(pad, 1e30, np.float32)])
+    Y0 = rng.normal(size=(n_tokens, N)).astype(np.float32) if y0 else None
+    dev = torch.device("cuda:0")
+    Xd = torch.from_numpy(X.view(np.int16)).to(dev).view(torch.bfloat16)
+    Bd = torch.from_numpy(w.B.view(np.int16)).to(dev).view(torch.bfloat16)
+    off = torch.from_numpy(w.offsets).to(dev)
+    Y = (torch.from_numpy(Y0).to(dev) if y0 else
+         torch.zeros((n_tokens, N), dtype=torch.float32, device=dev))
+    _say("case combine tokens=%d E=%d K=%d N=%d topk=%d bm=%d values=%s y0=%s drop=%d" % (
+        n_tokens, E, K, N, topk, bm, values, y0, drop))
+    gg.grouped_gemm_gather_combine(Xd, torch.from_numpy(src_full).to(dev), Bd, off,
+                                   torch.from_numpy(dst_full).to(dev),
+                                   torch.from_numpy(g_full).to(dev), out=Y, bm=bm)
+    torch.cuda.synchronize()
+    ref = oracle.grouped_gemm_combine(X, src_full, w.B, w.offsets, dst_full, g_full, n_tokens,
+                                      Y0=None if Y0 is None else Y0.astype(np.float64))
+    return Y.cpu().numpy(), ref, (X, src_full, w, dst_full, g_full)
+
+
+@pytest.mark.parametrize("bm", BMS)
+def test_combine_topk(gg, bm):
+    got, (Y, SW, AY, terms), _ = _combine_case(gg, 150, 8, 200, 520, 2, 51, bm)
+    parity.check_combine(got, Y, SW, AY, terms, "combine top-2")
+
+
+@pytest.mark.parametrize("bm", [0, 64])
+def test_combine_top8_accumulates_into_start_values(gg, bm):
+    got, (Y, SW, AY, terms), _ = _combine_case(gg, 64, 32, 256, 264, 8, 52, bm, y0=True, pad=9)
+    assert (terms == 9).all()
+    parity.check_combine(got, Y, SW, AY, terms, "combine top-8 into Y0")
+
+
+@pytest.mark.parametrize("bm", [0, 16, 256])
+def test_combine_integer_exact(gg, bm):
+    # integer inputs and weights in quarters: every product, weighted term and
+    # partial sum is exact in fp32, so the result is exact in any add order
+    pick = lambda rng, n: rng.choice([0.25, 0.5, 0.75, 1.0, -0.5, 2.0], size=n)
+    got, (Y, _, _, _), _ = _combine_case(gg, 90, 6, 512, 136, 3, 53, bm, values="int", weights=pick)
+    assert np.array_equal(got, Y)
+
+
+def test_combine_top1_unit_weight_equals_scatter(gg):
+    # 0 + 1 * c = c exactly: the combine of a top-1 routing with unit weights
+    # is the gather entry point's scattered output, bit for bit
+    ones = lambda rng, n: np.ones(n)
+    got, _, (X, src, w, dst, _) = _combine_case(gg, 200, 8, 328, 392, 1, 54, 0, weights=ones)
+    dev = torch.device("cuda:0")
+    C = torch.full((200, w.N), float("nan"), dtype=torch.float32, device=dev)
+    # every token has one route, so dst is a permutation of the token rows
+    gg.grouped_gemm_gather(torch.from_numpy(X.view(np.int16)).to(dev).view(torch.bfloat16),
+                           torch.from_numpy(src).to(dev),
+                           torch.from_numpy(w.B.view(np.int16)).to(dev).view(torch.bfloat16),
+                           torch.from_numpy(w.offsets).to(dev),
+                           dst_rows=torch.from_numpy(dst).to(dev), out=C[: w.M_cap], bm=0)
+    torch.cuda.synchronize()
+    assert np.array_equal(got, C.cpu().numpy())
+
+
+def test_combine_skips_out_of_range_destinations(gg):
+    got, (Y, SW, AY, terms), _ = _combine_case(gg, 80, 8, 136, 256, 2, 55, 0, y0=True, drop=17)
+    assert (terms < 3).any()
+    parity.check_combine(got, Y, SW, AY, terms, "combine with dropped routes")
+
+
+def test_combine_decode_shape(gg):
+    # 256 tokens, top-8 over 32 experts (2,048 routed rows), K = 2048, N = 1024
+    got, (Y, SW, AY, terms), _ = _combine_case(gg, 256, 32, 2048, 1024, 8, 56, 0)
+    parity.check_combine(got, Y, SW, AY, terms, "combine decode-like")
+
+
 # ---- fp8 weights with per-column scales ---------------------------------------------
 
 def _fp8_dev(w, Bq, scale):

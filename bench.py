@@ -69,14 +69,20 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(config, bm, out="fp32", weights="bf16"):
+def traffic_key(config, bm, out="fp32", weights="bf16", rows="grouped"):
+    """Key of a workload and entry point in profiles/traffic.json."""
+    return ("%s/bm%d" % (config, bm) + ("" if out == "fp32" else "/" + out)
+            + ("" if weights == "bf16" else "/%sw" % weights)
+            + ("" if rows == "grouped" else "/" + rows))
+
+
+def measured_traffic(config, bm, out="fp32", weights="bf16", rows="grouped"):
     """HBM bytes per launch from the committed counter summary, if still current."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     try:
-        key = ("%s/bm%d" % (config, bm) + ("" if out == "fp32" else "/" + out)
-               + ("" if weights == "bf16" else "/%sw" % weights))
+        key = traffic_key(config, bm, out, weights, rows)
         rec = json.load(open(path)).get(key)
     except (OSError, ValueError):
         return None
@@ -262,7 +268,8 @@ def main():
     intensity = useful / alg_bytes
     hbm_gbs = alg_bytes / launch_s / 1e9
     tflops_launch = useful / launch_s / 1e12
-    traffic = None if args.gather else measured_traffic(args.config, args.bm, args.out, args.weights)
+    rows_mode = "combine" if args.combine else "gather" if args.gather else "grouped"
+    traffic = measured_traffic(args.config, args.bm, args.out, args.weights, rows_mode)
     if intensity < RIDGE:
         roof = {"bound": "hbm", "achieved": round(hbm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(hbm_gbs / HBM_PEAK_GBS, 4), "traffic": traffic}

@@ -149,9 +149,9 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(expert-parallel sharding is described in DESIGN.md); run with --gpus 1",
-              file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path (each GPU "
+              "runs the kernel on its own experts' share; the exchanges sit outside it); "
+              "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

@@ -792,6 +792,39 @@ def test_graph_capture_replays(gg):
         torch.cuda.synchronize()
 
 
+def test_concurrent_streams(gg):
+    # the library keeps no mutable state per call: launches of different
+    # problems and entry points on two streams, queued without a sync between
+    # them, each match the single-stream result
+    w1 = wl.make_workload(E=6, K=328, N=392, sizes=[0, 1, 17, 130, 0, 300], seed=21, M_cap=470)
+    w2 = wl.make_workload(E=3, K=512, N=264, sizes=[200, 7, 0], seed=24)
+    A1, B1, off1 = _dev(w1)
+    A2, B2, off2 = _dev(w2)
+    want1 = gg.grouped_gemm(A1, B1, off1, bm=0)
+    want2 = gg.grouped_gemm(A2, B2, off2, bm=16, out_dtype=torch.bfloat16)
+    want3 = gg.grouped_gemm_swiglu(A2, B2, off2, bm=0)
+    torch.cuda.synchronize()
+    _say("case two streams")
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = []
+    for _ in range(3):
+        c1 = torch.full_like(want1, float("nan"))
+        c2 = torch.full_like(want2, float("nan"))
+        c3 = torch.full_like(want3, float("nan"))
+        torch.cuda.synchronize()
+        for _ in range(4):
+            gg.grouped_gemm(A1, B1, off1, out=c1, bm=0, stream=s1)
+            gg.grouped_gemm(A2, B2, off2, out=c2, bm=16, stream=s2)
+            gg.grouped_gemm_swiglu(A2, B2, off2, out=c3, bm=0, stream=s2)
+        outs.append((c1, c2, c3))
+    torch.cuda.synchronize()
+    for c1, c2, c3 in outs:
+        assert torch.equal(c1[: w1.M_tot], want1[: w1.M_tot])
+        assert torch.equal(c2[: w2.M_tot].view(torch.int16), want2[: w2.M_tot].view(torch.int16))
+        assert torch.equal(c3[: w2.M_tot].view(torch.int16), want3[: w2.M_tot].view(torch.int16))
+        assert torch.isnan(c1[w1.M_tot:]).all()
+
+
 # ---- edge shapes ---------------------------------------------------------------------
 
 @pytest.mark.parametrize("bm", [0, 16, 256])

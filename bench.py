@@ -113,13 +113,24 @@ def cpu_baseline(w, budget_s=12.0):
     dt1, _, _, _ = run(1)
     n = int(max(1, min(len(nz), budget_s / max(dt1, 1e-6))))
     dt, flops, rows, e1 = run(n)
+    # a whole workload that takes well under the budget is timed over
+    # repeated passes, so that the figure rests on about budget_s of work
+    passes = 1
+    while n == len(nz) and dt < 0.8 * budget_s:
+        more = int(min(50, max(1, (budget_s - dt) / max(dt / passes, 1e-6))))
+        for _ in range(more):
+            d, _, _, _ = run(n)
+            dt += d
+        passes += more
     return {
-        "value": flops / dt / 1e12,
+        "value": passes * flops / dt / 1e12,
         "unit": "TFLOP/s",
         "cores": oracle.threads(),
         "kind": "oracle",
-        "sample": "experts 0..%d of the %s workload (%d routed rows, full K=%d and N=%d), "
-                  "fp64 accumulation plus the sum|ab| bound, %.1f s" % (e1 - 1, w.name, rows, w.K, w.N, dt),
+        "sample": "%s of experts 0..%d of the %s workload (%d routed rows, full K=%d and N=%d), "
+                  "fp64 accumulation plus the sum|ab| bound, %.1f s in all" % (
+                      "%d passes" % passes if passes > 1 else "one pass", e1 - 1, w.name, rows,
+                      w.K, w.N, dt),
     }
 
 
@@ -281,6 +292,15 @@ def main():
     roof["algorithmic_bytes_per_launch"] = alg_bytes
     roof["avg_launch_us"] = round(launch_s * 1e6, 2)
 
+    # the device's tile list for this launch (untimed): tile count, tile
+    # heights and row efficiency eta = routed rows / scheduled rows
+    tiles, n_tiles = gg.tile_schedule(off, w.N, w.M_cap, bm=args.bm)
+    tl = tiles.cpu().numpy()
+    first = tl[tl[:, 3] == 0]  # one entry per M tile (its first column tile)
+    heights = {int(h): int((first[:, 4] == h).sum()) for h in sorted(set(first[:, 4].tolist()))}
+    schedule = {"tiles": int(n_tiles), "m_tiles": int(len(first)), "m_tiles_by_height": heights,
+                "eta": round(float(first[:, 2].sum()) / max(1.0, float(first[:, 4].sum())), 4)}
+
     cpu = None
     if not args.no_cpu_baseline:
         print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
@@ -310,6 +330,7 @@ def main():
         "hbm_frac": round(hbm_gbs / HBM_PEAK_GBS, 4),
         "mfma_frac": round(tflops_launch / MFMA_BF16_PEAK_TFLOPS, 4),
         "roofline": roof,
+        "schedule": schedule,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -232,7 +232,8 @@ gg_status_t gg_grouped_gemm_fp8w(const void *A, const void *Bq, const float *b_s
  * the worklog's; the order is expert by expert, and inside an expert the M
  * tiles are taken in groups of up to 8 with the N tile outer and the M tile
  * inner in each group (so consecutive tiles share a column slice of the
- * expert's weights). Tiles are 256 columns wide for every height. At most
+ * expert's weights). Tiles are 256 columns wide, except when every expert
+ * with rows has 16-row tiles: then they are 512 wide. At most
  * max_tiles descriptors are written; *n_tiles (a device int32) receives the
  * full count even when it exceeds max_tiles.
  * Arguments E, N, M_cap, bm and the offsets rules are those of

@@ -8,8 +8,9 @@
 //
 // MI355X mapping:
 //  * One workgroup of eight waves per CU (two waves per SIMD, at most 256
-//    registers per wave; up to 141 KiB of LDS). Every tile is 256 columns
-//    wide, so a tile's A rows are fetched once per 256 output columns. What
+//    registers per wave; up to 141 KiB of LDS). Tiles are 256 columns wide
+//    (512 for the 16-row tiles of a launch whose tiles are all 16 rows high),
+//    so a tile's A rows are fetched once per 256 output columns. What
 //    limits these kernels is how many bytes each CU's vector memory path
 //    (address unit and L1) keeps in flight against the L2/HBM latency, so the
 //    design minimises the bytes each CU must fetch (wide tiles, 128-byte row
@@ -38,9 +39,10 @@
 
 namespace gg {
 
-template <int BM_, int BK_, int WM_, int WN_, int AD_, int BD_, bool FP8B_ = false, int NS_ = 2>
+template <int BM_, int BK_, int WM_, int WN_, int AD_, int BD_, bool FP8B_ = false, int NS_ = 2,
+          int BN_ = kTileN>
 struct TileCfg {
-  static constexpr int BM = BM_, BN = width_of(BM_), BK = BK_, WM = WM_, WN = WN_;
+  static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_;
   // K slices of A and of B held in registers ahead of the LDS stage
   static constexpr int AD = AD_, BD = BD_;
   // LDS stages: 2 = the next slice is written while the current one is read
@@ -70,8 +72,10 @@ struct TileCfg {
   static constexpr int LDS_BYTES = NS * (A_STAGE + B_STAGE) * 2;
 };
 
-// Tile configurations per tile height (all 256 columns wide; eight waves).
+// Tile configurations per tile height (256 columns wide, and 512 for the
+// 16-row tiles of launches whose tiles are all 16 rows high; eight waves).
 using Cfg16 = TileCfg<16, 64, 1, 8, 1, 2>;    // wave tile 16 x 32
+using Cfg16W = TileCfg<16, 64, 1, 8, 1, 2, false, 2, kWideN>;  // wave tile 16 x 64
 using Cfg32 = TileCfg<32, 64, 1, 8, 1, 2>;    // wave tile 32 x 32
 using Cfg64 = TileCfg<64, 64, 1, 8, 1, 2>;    // wave tile 64 x 32
 using Cfg128 = TileCfg<128, 64, 2, 4, 1, 2>;  // wave tile 64 x 64
@@ -81,6 +85,7 @@ using Cfg256 = TileCfg<256, 64, 2, 4, 1, 2>;  // wave tile 128 x 64
 // bytes of a bf16 one; the weight-streaming heights take 128-deep slices so
 // that each CU keeps as many weight bytes in flight as with bf16.
 using Cfg16F = TileCfg<16, 128, 1, 8, 1, 2, true>;
+using Cfg16FW = TileCfg<16, 64, 1, 8, 1, 2, true, 2, kWideN>;  // 512 wide: a 64-deep slice
 using Cfg32F = TileCfg<32, 128, 1, 8, 1, 2, true>;
 using Cfg64F = TileCfg<64, 64, 1, 8, 1, 2, true>;
 using Cfg128F = TileCfg<128, 64, 2, 4, 1, 2, true>;

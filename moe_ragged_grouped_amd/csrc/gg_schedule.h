@@ -28,12 +28,20 @@ namespace gg {
 constexpr int kMaxExperts = 1024;  // the tile prefix lives in LDS
 constexpr int kGroupM = 8;         // M tiles per group in the within-expert order
 
-// Tile heights this library runs, smallest first; every tile is kTileN
-// columns wide.
+// Tile heights this library runs, smallest first. Tiles are kTileN columns
+// wide, except in a launch where every expert's tiles are 16 rows high (the
+// weight-streaming decode case): there the tiles are kWideN wide, so each
+// workgroup streams twice the contiguous weight row per slice and a launch
+// has half as many tiles (measured on 32 experts x 16 rows, K=6144,
+// N=4096: 242 -> 237 us). In launches that mix heights, 16-row tiles stay
+// narrow: wide ones there become the long poles of the launch.
 constexpr int kNumHeights = 5;
 constexpr int kTileN = 256;
+constexpr int kWideN = 512;
 __host__ __device__ constexpr int height_of(int cls) { return 16 << cls; }
-__host__ __device__ constexpr int width_of(int) { return kTileN; }
+__host__ __device__ constexpr int width_of(int bm, bool wide16) {
+  return (bm == 16 && wide16) ? kWideN : kTileN;
+}
 
 // Per-expert tile height when the caller leaves the choice to the device.
 // Minimises ceil(m/BM) * (BM + 64) over BM in {16, 32, 64, 128, 256}: the
@@ -60,13 +68,15 @@ struct Tile {
   int row0;   // first row in A and C
   int rows;   // valid rows, 1..bm
   int col0;   // first column in C
-  int bm;     // tile height (the width is width_of(bm))
+  int bm;     // tile height
+  int bn;     // tile width: width_of(bm, the launch's wide16 flag)
 };
 
 // LDS table: exclusive prefix of tile counts per expert (start[E] = total).
 struct SchedLds {
   int start[kMaxExperts + 1];
   int wave_sum[kThreads / kWave];
+  int wide16;  // every expert with rows has 16-row tiles: they are kWideN wide
 };
 
 // Clamped group boundaries: every offset is pulled into [0, M_cap].
@@ -83,24 +93,29 @@ __device__ inline int build_schedule(SchedLds &s, const int32_t *__restrict__ of
   // each thread owns a run of consecutive experts (E <= 1024 -> at most 2)
   constexpr int kRun = kMaxExperts / kThreads;
   const int e0 = tid * kRun;
-  int cnt[kRun];
-  int local = 0;
+  int rows[kRun], height[kRun];
+  int tall = 0;  // an expert of this run has rows and taller tiles than 16
   int lo = e0 < E ? clamp_off(off_g, e0, M_cap) : 0;
 #pragma unroll
   for (int j = 0; j < kRun; ++j) {
     const int e = e0 + j;
-    int c = 0;
+    rows[j] = 0;
+    height[j] = 16;
     if (e < E) {
       const int hi = clamp_off(off_g, e + 1, M_cap);
-      const int m = hi - lo;
-      if (m > 0) {
-        const int b = bm_fixed ? bm_fixed : adaptive_bm(m);
-        c = cdiv(m, b) * cdiv(N, width_of(b));
-      }
+      rows[j] = hi > lo ? hi - lo : 0;
+      height[j] = bm_fixed ? bm_fixed : adaptive_bm(rows[j]);
+      tall |= rows[j] > 0 && height[j] > 16;
       lo = hi;
     }
-    cnt[j] = c;
-    local += c;
+  }
+  const bool wide16 = !__syncthreads_or(tall);
+  int cnt[kRun];
+  int local = 0;
+#pragma unroll
+  for (int j = 0; j < kRun; ++j) {
+    cnt[j] = rows[j] > 0 ? cdiv(rows[j], height[j]) * cdiv(N, width_of(height[j], wide16)) : 0;
+    local += cnt[j];
   }
   // inclusive scan of 'local' across the 64 lanes of the wave
   const int lane = tid % kWave, wave = tid / kWave;
@@ -126,7 +141,10 @@ __device__ inline int build_schedule(SchedLds &s, const int32_t *__restrict__ of
   int total = 0;
 #pragma unroll
   for (int w = 0; w < kThreads / kWave; ++w) total += s.wave_sum[w];
-  if (tid == 0) s.start[E] = total;
+  if (tid == 0) {
+    s.start[E] = total;
+    s.wide16 = wide16;
+  }
   __syncthreads();
   return total;
 }
@@ -142,7 +160,7 @@ __device__ __forceinline__ Tile decode_tile(const SchedLds &s, const int32_t *__
   const int r0 = clamp_off(off_g, lo, M_cap);
   const int m = clamp_off(off_g, lo + 1, M_cap) - r0;
   const int b = bm_fixed ? bm_fixed : adaptive_bm(m);
-  const int bn = width_of(b);
+  const int bn = width_of(b, s.wide16 != 0);
   const int NT = cdiv(N, bn);
   const int n_mt = cdiv(m, b);
   const int local = t - s.start[lo];
@@ -156,6 +174,7 @@ __device__ __forceinline__ Tile decode_tile(const SchedLds &s, const int32_t *__
   Tile tl;
   tl.expert = lo;
   tl.bm = b;
+  tl.bn = bn;
   tl.row0 = r0 + mt * b;
   tl.rows = min(b, m - mt * b);
   tl.col0 = nt * bn;

@@ -138,7 +138,12 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(Params p) {
     if (t >= total) break;
     const Tile tl = decode_tile(sched, p.off, t, p.E, p.M_cap, p.N, p.bm_fixed);
     switch (tl.bm) {
-      case 16: if constexpr (MASK & 1) tile_call<Pick<F8, Cfg16, Cfg16F>, O, R>(p, tl, lds); break;
+      case 16:
+        if constexpr (MASK & 1) {
+          if (tl.bn == kWideN) tile_call<Pick<F8, Cfg16W, Cfg16FW>, O, R>(p, tl, lds);
+          else tile_call<Pick<F8, Cfg16, Cfg16F>, O, R>(p, tl, lds);
+        }
+        break;
       case 32: if constexpr (MASK & 2) tile_call<Pick<F8, Cfg32, Cfg32F>, O, R>(p, tl, lds); break;
       case 64: if constexpr (MASK & 4) tile_call<Pick<F8, Cfg64, Cfg64F>, O, R>(p, tl, lds); break;
       case 128:
@@ -175,6 +180,7 @@ template <int MASK, bool F8>
 constexpr int lds_bytes() {
   int m = 0;
   if (MASK & 1) m = m > Pick<F8, Cfg16, Cfg16F>::LDS_BYTES ? m : Pick<F8, Cfg16, Cfg16F>::LDS_BYTES;
+  if (MASK & 1) m = m > Pick<F8, Cfg16W, Cfg16FW>::LDS_BYTES ? m : Pick<F8, Cfg16W, Cfg16FW>::LDS_BYTES;
   if (MASK & 2) m = m > Pick<F8, Cfg32, Cfg32F>::LDS_BYTES ? m : Pick<F8, Cfg32, Cfg32F>::LDS_BYTES;
   if (MASK & 4) m = m > Pick<F8, Cfg64, Cfg64F>::LDS_BYTES ? m : Pick<F8, Cfg64, Cfg64F>::LDS_BYTES;
   if (MASK & 8)

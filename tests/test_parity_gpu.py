@@ -163,7 +163,7 @@ def test_tile_schedule_matches_oracle(gg, sizes, bm, N):
     _say("case schedule %s bm=%d N=%d" % (sizes, bm, N))
     tiles, n = gg.tile_schedule(torch.from_numpy(off).cuda(), N, M_cap, bm)
     hs = oracle.adaptive_bm(sizes) if bm == 0 else [bm] * len(sizes)
-    ws = [gg.TILE_WIDTH[h] for h in hs]
+    ws = gg.tile_widths(hs, sizes)
     ref = oracle.tile_list(off, N, hs, ws)
     assert n == len(ref)
     got = [tuple(int(v) for v in r) for r in tiles.cpu().numpy()]

@@ -75,7 +75,10 @@ struct TileCfg {
 // Tile configurations per tile height (256 columns wide, and 512 for the
 // 16-row tiles of launches whose tiles are all 16 rows high; eight waves).
 using Cfg16 = TileCfg<16, 64, 1, 8, 1, 2>;    // wave tile 16 x 32
-using Cfg16W = TileCfg<16, 64, 1, 8, 1, 2, false, 2, kWideN>;  // wave tile 16 x 64
+// 512 wide, B one slice ahead: a 64 KB slice per CU is already enough in
+// flight (measured on the decode shape: one slice ahead 234 us, two 237,
+// three 239; fp8 weights, half the bytes per slice, want two).
+using Cfg16W = TileCfg<16, 64, 1, 8, 1, 1, false, 2, kWideN>;  // wave tile 16 x 64
 using Cfg32 = TileCfg<32, 64, 1, 8, 1, 2>;    // wave tile 32 x 32
 using Cfg64 = TileCfg<64, 64, 1, 8, 1, 2>;    // wave tile 64 x 32
 using Cfg128 = TileCfg<128, 64, 2, 4, 1, 2>;  // wave tile 64 x 64

@@ -331,13 +331,14 @@ def test_bf16_out_is_fp32_out_rounded(gg, bm):
     assert torch.equal(c32[:m].cpu().to(torch.bfloat16).view(torch.int16), c16[:m].cpu().view(torch.int16))
 
 
-def test_bf16_out_full_size_sampled(gg):
-    w = _full("uniform16k")
+@pytest.mark.parametrize("name", ["decode", "uniform16k"])
+def test_bf16_out_full_size_sampled(gg, name):
+    w = _full(name)
     guard = 16
     dev = torch.device("cuda:0")
     A, B, off = _dev(w)
     Cbig = torch.full((w.M_cap + guard, w.N), float("nan"), dtype=torch.bfloat16, device=dev)
-    _say("case bf16-out full uniform16k")
+    _say("case bf16-out full %s" % name)
     gg.grouped_gemm(A, B, off, out=Cbig[: w.M_cap], bm=0)
     torch.cuda.synchronize()
     out = Cbig.float().cpu().numpy().astype(np.float64)
@@ -346,7 +347,7 @@ def test_bf16_out_full_size_sampled(gg):
     rng = np.random.default_rng(8)
     rows, cols = _samples(w, rng)
     c, s = oracle.grouped_gemm_entries(w.A, w.B, w.offsets, rows, cols)
-    parity.check_bf16(out[rows, cols], c, s, "uniform16k bf16 sampled")
+    parity.check_bf16(out[rows, cols], c, s, name + " bf16 sampled")
 
 
 # ---- SwiGLU of (gate, up) column pairs, bf16 output --------------------------------
@@ -411,13 +412,14 @@ def test_swiglu_is_activated_fp32_product(gg, bm):
     assert (got <= oracle.round_to_bf16(h64 + slack)).all()
 
 
-def test_swiglu_full_size_sampled(gg):
-    w = _full("uniform16k")
+@pytest.mark.parametrize("name", ["decode", "uniform16k"])
+def test_swiglu_full_size_sampled(gg, name):
+    w = _full(name)
     guard = 16
     dev = torch.device("cuda:0")
     A, B, off = _dev(w)
     Hbig = torch.full((w.M_cap + guard, w.N // 2), float("nan"), dtype=torch.bfloat16, device=dev)
-    _say("case swiglu full uniform16k")
+    _say("case swiglu full %s" % name)
     gg.grouped_gemm_swiglu(A, B, off, out=Hbig[: w.M_cap], bm=0)
     torch.cuda.synchronize()
     out = Hbig.float().cpu().numpy().astype(np.float64)
@@ -430,7 +432,7 @@ def test_swiglu_full_size_sampled(gg):
     cc = np.stack([2 * pairs, 2 * pairs + 1], axis=1).ravel()
     c, s = oracle.grouped_gemm_entries(w.A, w.B, w.offsets, rr, cc)
     parity.check_swiglu_bf16(out[rows, pairs][:, None], c.reshape(-1, 2), s.reshape(-1, 2),
-                             "uniform16k swiglu sampled")
+                             name + " swiglu sampled")
 
 
 # ---- rows gathered / scattered by index -------------------------------------------
@@ -647,6 +649,35 @@ def test_combine_skips_out_of_range_destinations(gg):
     got, (Y, SW, AY, terms), _ = _combine_case(gg, 80, 8, 136, 256, 2, 55, 0, y0=True, drop=17)
     assert (terms < 3).any()
     parity.check_combine(got, Y, SW, AY, terms, "combine with dropped routes")
+
+
+def test_combine_full_decode_sampled(gg):
+    # the benchmark's combine launch: the decode workload's rows reached
+    # through a seeded top-1 permutation, gate weights in (0.05, 1], Y
+    # accumulated into from a nonzero start; sampled rows against the oracle
+    w = _full("decode")
+    rng = np.random.default_rng(w.seed + 500)
+    perm = rng.permutation(w.M_cap).astype(np.int32)
+    gate = rng.uniform(0.05, 1.0, w.M_cap).astype(np.float32)
+    dev = torch.device("cuda:0")
+    A, B, off = _dev(w)
+    X = torch.empty_like(A)
+    X[torch.from_numpy(perm).long().to(dev)] = A  # grouped row r is token row perm[r]
+    Y0 = torch.full((w.M_cap, w.N), 0.5, dtype=torch.float32, device=dev)
+    Y = Y0.clone()
+    _say("case combine full decode")
+    pd = torch.from_numpy(perm).to(dev)
+    gg.grouped_gemm_gather_combine(X, pd, B, off, pd, torch.from_numpy(gate).to(dev), out=Y, bm=0)
+    torch.cuda.synchronize()
+    out = Y.cpu().numpy()
+    assert np.isfinite(out).all()
+    rows, cols = _samples(w, np.random.default_rng(10))
+    c, s = oracle.grouped_gemm_entries(w.A, w.B, w.offsets, rows, cols)
+    # top-1: Y[perm[r]] = 0.5 + gate[r] * C[r], one product and one add
+    want = 0.5 + gate[rows].astype(np.float64) * c
+    bound = parity.ELEM * np.abs(gate[rows]) * s + 3 * 2.0 ** -23 * (0.5 + np.abs(gate[rows] * c))
+    got = out[perm[rows], cols]
+    assert (np.abs(got - want) <= bound).all(), float(np.max(np.abs(got - want) / bound))
 
 
 def test_combine_decode_shape(gg):

@@ -29,7 +29,9 @@ up pairs, bf16 H of N/2 columns written); its output counts at 1 byte per
 product column. --gather and --combine time the entry points that reach rows
 by index (a seeded top-1 permutation); --combine adds weight * row into fp32
 output rows with atomics, counted as a read and a write of every output
-element.
+element. --weights fp8 times fp8 weights with bf16 activations (widened to
+bf16 before the matrix cores); --weights fp8 --acts fp8 times fp8 activations
+and weights on the fp8 matrix cores, against the fp8 peak (5.0 PFLOP/s).
 """
 
 import argparse
@@ -46,7 +48,7 @@ if ROOT not in sys.path:
 METRIC = "useful TFLOP/s (2*M_tot*K*N/t) + HBM GB/s, % of roofline, 1 MI355X"
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
-RIDGE = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)  # flop per byte
+MFMA_FP8_PEAK_TFLOPS = 5000.0
 KERNEL_NAME = "grouped_gemm_kernel"
 
 DESCRIPTIONS = {
@@ -147,6 +149,9 @@ def main():
     ap.add_argument("--out", default="fp32", choices=("fp32", "bf16", "swiglu"),
                     help="what the epilogue writes: fp32 C, bf16 C, or bf16 SwiGLU of "
                          "(gate, up) column pairs")
+    ap.add_argument("--acts", default="bf16", choices=("bf16", "fp8"),
+                    help="activations: bf16, or fp8 E4M3 with per-row scales (needs "
+                         "--weights fp8; fp8 matrix cores)")
     ap.add_argument("--weights", default="bf16", choices=("bf16", "fp8"),
                     help="fp8: E4M3 weights with per-column scales (a separate precision)")
     ap.add_argument("--gather", action="store_true",
@@ -202,6 +207,12 @@ def main():
         Bq = torch.from_numpy(q_np).to(dev)
         Bs = torch.from_numpy(sc_np).to(dev)
         del q_np
+    if args.acts == "fp8":
+        if args.weights != "fp8":
+            raise SystemExit("--acts fp8 needs --weights fp8")
+        aq_np, as_np = wl.fp8_activations(w)
+        Aq = torch.from_numpy(aq_np).to(dev)
+        As = torch.from_numpy(as_np).to(dev)
     if args.combine:
         args.gather = True
     if args.gather:
@@ -223,7 +234,9 @@ def main():
             C.zero_()
 
     def step():
-        if args.weights == "fp8":
+        if args.acts == "fp8":
+            gg.grouped_gemm_fp8(Aq, As, Bq, Bs, off, out=C, bm=args.bm)
+        elif args.weights == "fp8":
             gg.grouped_gemm_fp8w(A, Bq, Bs, off, out=C, bm=args.bm)
         elif args.combine:
             gg.grouped_gemm_gather_combine(X, perm, B, off, perm, gate, out=C, bm=args.bm)
@@ -272,7 +285,8 @@ def main():
     c_bytes = {"fp32": 4, "bf16": 2, "swiglu": 1}[args.out]  # per product column
     active = int((w.sizes > 0).sum())
     b_bytes = 2 * w.K * w.N * active if args.weights == "bf16" else (w.K + 4) * w.N * active
-    alg_bytes = (2 * w.M_tot * w.K + b_bytes + c_bytes * w.M_tot * w.N
+    a_bytes = 2 * w.M_tot * w.K if args.acts == "bf16" else (w.K + 4) * w.M_tot
+    alg_bytes = (a_bytes + b_bytes + c_bytes * w.M_tot * w.N
                  + (8 * w.M_tot if args.gather else 0)
                  # the combine reads each Y element before adding, and reads a weight per row
                  + (4 * w.M_tot * w.N + 4 * w.M_tot if args.combine else 0))
@@ -280,13 +294,18 @@ def main():
     hbm_gbs = alg_bytes / launch_s / 1e9
     tflops_launch = useful / launch_s / 1e12
     rows_mode = "combine" if args.combine else "gather" if args.gather else "grouped"
-    traffic = measured_traffic(args.config, args.bm, args.out, args.weights, rows_mode)
-    if intensity < RIDGE:
+    weights_key = "fp8a" if args.acts == "fp8" else args.weights
+    traffic = measured_traffic(args.config, args.bm, args.out, weights_key, rows_mode)
+    # the matrix-core peak of the operand type: fp8 x fp8 on the fp8 cores,
+    # otherwise bf16 (fp8 weights are widened to bf16 before the matrix cores)
+    mfma_peak = MFMA_FP8_PEAK_TFLOPS if args.acts == "fp8" else MFMA_BF16_PEAK_TFLOPS
+    ridge = mfma_peak * 1e12 / (HBM_PEAK_GBS * 1e9)  # flop per byte
+    if intensity < ridge:
         roof = {"bound": "hbm", "achieved": round(hbm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(hbm_gbs / HBM_PEAK_GBS, 4), "traffic": traffic}
     else:
-        roof = {"bound": "mfma", "achieved": round(tflops_launch, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(tflops_launch / MFMA_BF16_PEAK_TFLOPS, 4),
+        roof = {"bound": "mfma", "achieved": round(tflops_launch, 1), "peak": mfma_peak,
+                "unit": "TFLOP/s", "frac": round(tflops_launch / mfma_peak, 4),
                 "traffic": traffic}
     roof["kernel"] = KERNEL_NAME
     roof["algorithmic_bytes_per_launch"] = alg_bytes
@@ -318,17 +337,20 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if args.weights == "bf16" else "fp8w-bf16",
+        "dtype": ("fp8" if args.acts == "fp8" else "bf16" if args.weights == "bf16"
+                  else "fp8w-bf16"),
         "data": "synthetic (seeded normal draws rounded to bf16, no dataset)",
         "config": {"workload": DESCRIPTIONS[args.config], "name": args.config, "E": w.E, "K": w.K,
                    "N": w.N, "M_tot": w.M_tot, "bm": args.bm or "per-expert", "out_dtype": args.out,
                    "rows": ("gathered, weighted combine by fp32 atomics" if args.combine else
                             "gathered/scattered by index" if args.gather else "grouped"),
                    "weights": "bf16" if args.weights == "bf16"
-                   else "fp8 e4m3 + fp32 scale per expert column"},
+                   else "fp8 e4m3 + fp32 scale per expert column",
+                   "activations": "bf16" if args.acts == "bf16"
+                   else "fp8 e4m3 + fp32 scale per row"},
         "hbm_gbs": round(hbm_gbs, 1),
         "hbm_frac": round(hbm_gbs / HBM_PEAK_GBS, 4),
-        "mfma_frac": round(tflops_launch / MFMA_BF16_PEAK_TFLOPS, 4),
+        "mfma_frac": round(tflops_launch / mfma_peak, 4),
         "roofline": roof,
         "schedule": schedule,
         "cpu_baseline": cpu,

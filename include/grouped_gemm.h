@@ -220,6 +220,32 @@ gg_status_t gg_grouped_gemm_fp8w(const void *A, const void *Bq, const float *b_s
                                  int32_t N, int32_t M_cap, int32_t bm, void *stream);
 
 /*
+ * gg_grouped_gemm_fp8 -- fp8 activations and fp8 weights on the fp8 matrix
+ * cores (the article's FP8 scheme, read as one scale per activation row and
+ * one per weight column).
+ *
+ *   C[r][n] = a_scale[r] * b_scale[e][n] * sum_k dec(Aq[r][k]) * dec(Bq[e][k][n])
+ *
+ *   Aq       uint8 [M_cap][K], row-major, 16-byte aligned: E4M3 codes, rows
+ *            grouped by expert as A in gg_grouped_gemm_bf16.
+ *   a_scale  fp32 [M_cap] on the device, 4-byte aligned: one scale per row.
+ *   Bq       uint8 [E][K][N], 16-byte aligned: E4M3 codes, as for
+ *            gg_grouped_gemm_fp8w.
+ *   b_scale  fp32 [E][N], 16-byte aligned: one scale per expert and column.
+ *   C        fp32 [M_cap][N].
+ *   K and N must be multiples of 16 (GG_ERR_MISALIGNED otherwise).
+ * The products of two E4M3 values are exact; they accumulate in fp32 in the
+ * matrix cores (v_mfma_scale_f32_16x16x128_f8f6f4 with unit block scales),
+ * and the epilogue multiplies by the row and the column scale (two fp32
+ * roundings). Other arguments and rules are those of gg_grouped_gemm_bf16;
+ * a NULL scale pointer is GG_ERR_INVALID_VALUE.
+ */
+gg_status_t gg_grouped_gemm_fp8(const void *Aq, const float *a_scale, const void *Bq,
+                                const float *b_scale, const int32_t *group_offsets, float *C,
+                                int32_t E, int32_t K, int32_t N, int32_t M_cap, int32_t bm,
+                                void *stream);
+
+/*
  * gg_tile_schedule -- the flat tile list the product kernel consumes,
  * written out (worklog section 2: one descriptor per output tile of one
  * expert, expert-major order, tiles stopping at expert boundaries, empty

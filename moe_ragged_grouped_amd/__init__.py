@@ -14,7 +14,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["grouped_gemm", "grouped_gemm_swiglu", "grouped_gemm_gather", "grouped_gemm_gather_combine", "grouped_gemm_fp8w", "tile_schedule", "library_path", "load_library", "GroupedGemmError",
+__all__ = ["grouped_gemm", "grouped_gemm_swiglu", "grouped_gemm_gather", "grouped_gemm_gather_combine", "grouped_gemm_fp8w", "grouped_gemm_fp8", "tile_schedule", "library_path", "load_library", "GroupedGemmError",
            "BM_CHOICES", "TILE_N", "TILE_N_WIDE", "tile_widths", "MAX_EXPERTS", "SYMBOLS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -33,7 +33,7 @@ def tile_widths(heights, sizes):
 MAX_EXPERTS = 1024
 SYMBOLS = ("gg_grouped_gemm_bf16", "gg_grouped_gemm_bf16_bf16out", "gg_grouped_gemm_bf16_swiglu",
            "gg_grouped_gemm_bf16_gather", "gg_grouped_gemm_bf16_gather_combine",
-           "gg_grouped_gemm_fp8w", "gg_tile_schedule", "gg_status_string")
+           "gg_grouped_gemm_fp8w", "gg_grouped_gemm_fp8", "gg_tile_schedule", "gg_status_string")
 
 _lib = None
 
@@ -69,6 +69,8 @@ def load_library():
         lib.gg_grouped_gemm_bf16_gather_combine.restype = ctypes.c_int
         lib.gg_grouped_gemm_fp8w.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
         lib.gg_grouped_gemm_fp8w.restype = ctypes.c_int
+        lib.gg_grouped_gemm_fp8.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
+        lib.gg_grouped_gemm_fp8.restype = ctypes.c_int
         lib.gg_tile_schedule.argtypes = [vp, i32, i32, i32, i32, vp, vp, i32, vp]
         lib.gg_tile_schedule.restype = ctypes.c_int
         lib.gg_status_string.argtypes = [ctypes.c_int]
@@ -278,6 +280,42 @@ def grouped_gemm_fp8w(A, Bq, b_scale, offsets, out=None, bm: int = 0, stream=Non
                                   out.data_ptr(), E, K, N, M_cap, int(bm),
                                   _stream_handle(A.device, stream))
     _check(st, "gg_grouped_gemm_fp8w")
+    return out
+
+
+def grouped_gemm_fp8(Aq, a_scale, Bq, b_scale, offsets, out=None, bm: int = 0, stream=None):
+    """C = (a_scale * dec(Aq)) @ (dec(Bq[e]) * b_scale[e]) per expert, fp8 matrix cores.
+
+    Aq: uint8 [M_cap, K] E4M3 codes; a_scale: fp32 [M_cap]; Bq: uint8
+    [E, K, N] E4M3 codes; b_scale: fp32 [E, N]; offsets int32 [E+1]; out:
+    optional fp32 [M_cap, N]. K and N must be multiples of 16.
+    """
+    import torch
+    lib = load_library()
+    if Aq.dtype != torch.uint8 or Bq.dtype != torch.uint8:
+        raise TypeError("Aq and Bq must be uint8 E4M3 codes")
+    if a_scale.dtype != torch.float32 or b_scale.dtype != torch.float32:
+        raise TypeError("a_scale and b_scale must be float32")
+    if offsets.dtype != torch.int32:
+        raise TypeError("offsets must be int32")
+    if Aq.dim() != 2 or Bq.dim() != 3 or a_scale.dim() != 1 or b_scale.dim() != 2:
+        raise ValueError("shapes: Aq [M_cap,K], a_scale [M_cap], Bq [E,K,N], b_scale [E,N]")
+    tensors = [Aq, a_scale, Bq, b_scale, offsets]
+    if not all(t.is_cuda and t.is_contiguous() for t in tensors):
+        raise ValueError("all tensors must be contiguous device tensors")
+    E, K, N = Bq.shape
+    M_cap = Aq.shape[0]
+    if (Aq.shape[1] != K or a_scale.shape[0] != M_cap or tuple(b_scale.shape) != (E, N)
+            or offsets.shape[0] != E + 1):
+        raise ValueError("shape mismatch")
+    if out is None:
+        out = torch.empty((M_cap, N), dtype=torch.float32, device=Aq.device)
+    elif out.dtype != torch.float32 or tuple(out.shape) != (M_cap, N) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous fp32 [M_cap, N] tensor")
+    st = lib.gg_grouped_gemm_fp8(Aq.data_ptr(), a_scale.data_ptr(), Bq.data_ptr(),
+                                 b_scale.data_ptr(), offsets.data_ptr(), out.data_ptr(), E, K, N,
+                                 M_cap, int(bm), _stream_handle(Aq.device, stream))
+    _check(st, "gg_grouped_gemm_fp8")
     return out
 
 

@@ -49,9 +49,11 @@ struct TileCfg {
   // (one barrier per slice); 1 = write after a second barrier (half the LDS)
   static constexpr int NS = NS_;
   static_assert(NS == 1 || NS == 2, "LDS stages");
+  static constexpr bool Q8 = false;  // bf16 activations (see gg_mainloop_q8.h)
   // B in HBM: bf16 (2 bytes) or fp8 e4m3 (1 byte, widened to bf16 on its way
   // into LDS); one 16-byte global chunk holds B_CE elements of a B row
   static constexpr bool FP8B = FP8B_;
+  static constexpr int A_ELEM = 2;  // bytes per A element (bf16)
   static constexpr int B_ELEM = FP8B ? 1 : 2;
   static constexpr int B_CE = 16 / B_ELEM;
   static_assert(WM * WN == kThreads / kWave, "one wave per wave tile");
@@ -101,13 +103,14 @@ using Cfg256F = TileCfg<256, 64, 2, 4, 1, 2, true>;
 enum class Rows { Grouped, Indexed };
 
 struct TileArgs {
-  const uint16_t *A;   // Grouped: A rows of this tile (row r at A + r * K); Indexed: X
+  const void *A;       // Grouped: A rows of this tile (row r at A + r * K); Indexed: X
   const char *B;       // B[e] + col0: element (k, n) at byte (k * N + n) * B_ELEM
   void *C;             // C + row0 * N + col0 (C + col0 when dst is given); for SwiGLU
                        // output H + row0 * N/2 + col0/2
   int rows, K, N, ncols;  // ncols = valid columns in this tile (<= BN)
   long long b_bytes;   // bytes from B to the end of B[e]: (K * N - col0) * B_ELEM
   const float *scale;  // fp8 B: scale[e][col0 ..], one per output column; else null
+  const float *a_scale;  // fp8 A: a_scale[row0 ..], one per row; else null
   int tid;             // threadIdx.x, re-derived per tile (see tile_body)
   // Indexed rows only
   const int32_t *src;  // src_rows + row0

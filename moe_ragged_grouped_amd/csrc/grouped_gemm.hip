@@ -19,6 +19,7 @@
 #include "grouped_gemm.h"  // include/ (on the -I path)
 #include "gg_common.h"
 #include "gg_mainloop.h"
+#include "gg_mainloop_q8.h"
 #include "gg_schedule.h"
 
 #include <mutex>
@@ -28,8 +29,13 @@ namespace gg {
 
 constexpr int kXcds = 8;
 
-template <bool F8, class Bf16Cfg, class Fp8Cfg>
-using Pick = typename std::conditional<F8, Fp8Cfg, Bf16Cfg>::type;
+// Operand precisions: bf16 A and B; bf16 A with fp8 weights (widened to
+// bf16 on their way into LDS); fp8 A and B on the fp8 matrix cores.
+enum Prec : int { kBf16 = 0, kW8 = 1, kW8A8 = 2 };
+
+template <int P, class Bf16Cfg, class W8Cfg, class Q8Cfg>
+using Pick = typename std::conditional<
+    P == kW8A8, Q8Cfg, typename std::conditional<P == kW8, W8Cfg, Bf16Cfg>::type>::type;
 constexpr int kMaxK = 1 << 22;
 constexpr int kMaxN = 1 << 24;
 
@@ -45,6 +51,7 @@ struct Params {
   const int32_t *dst_rows;  // [M_cap] or null: grouped row r writes C row dst_rows[r]
   int n_src;                // rows of A in the indexed form
   const float *b_scale;     // fp8 weights only: [E][N] per-column scales
+  const float *a_scale;     // fp8 activations only: [M_cap] per-row scales
   int n_dst;                // indexed form: rows of C (M_cap, or the combine's n_dst)
   const float *row_w;       // combine only: [M_cap] weight of each grouped row
 };
@@ -79,17 +86,18 @@ __device__ __forceinline__ void tile_body(const Params &p, int row0, int rows, i
   a.B = (const char *)uniform_ptr(B) + ((size_t)expert * K * N + col0) * Cfg::B_ELEM;
   a.scale = Cfg::FP8B ? (const float *)uniform_ptr(p.b_scale) + (size_t)expert * N + col0
                       : nullptr;
+  a.a_scale = Cfg::Q8 ? (const float *)uniform_ptr(p.a_scale) + row0 : nullptr;
   // bytes per C element, and C elements per product column (SwiGLU writes one
   // bf16 per (gate, up) pair)
   constexpr size_t kOutBytes = (O == Out::F32 || O == Out::AddF32) ? 4 : 2;
   constexpr int kColsPerOut = O == Out::SwiGluBF16 ? 2 : 1;
   if constexpr (R == Rows::Grouped) {
-    a.A = (const uint16_t *)uniform_ptr(A) + (size_t)row0 * K;
+    a.A = (const char *)uniform_ptr(A) + (size_t)row0 * K * Cfg::A_ELEM;
     a.C = (char *)uniform_ptr(C) + ((size_t)row0 * N + col0) / kColsPerOut * kOutBytes;
     a.src = a.dst = nullptr;
     a.n_src = a.n_dst = 0;
   } else {
-    a.A = (const uint16_t *)uniform_ptr(A);
+    a.A = uniform_ptr(A);
     a.src = (const int32_t *)uniform_ptr(p.src_rows) + row0;
     const int32_t *dst = (const int32_t *)uniform_ptr(p.dst_rows);
     a.dst = dst ? dst + row0 : nullptr;
@@ -109,7 +117,12 @@ __device__ __forceinline__ void tile_body(const Params &p, int row0, int rows, i
   int tid = threadIdx.x;
   asm volatile("" : "+v"(tid));
   a.tid = tid;
-  run_tile<Cfg, O, R>(a, lds);
+  if constexpr (Cfg::Q8) {
+    static_assert(O == Out::F32 && R == Rows::Grouped, "fp8 activations: grouped rows, fp32 C");
+    run_tile_q8<Cfg>(a, lds);
+  } else {
+    run_tile<Cfg, O, R>(a, lds);
+  }
 }
 
 template <class Cfg, Out O, Rows R>
@@ -120,8 +133,9 @@ __device__ __forceinline__ void tile_call(const Params &p, const Tile &t, uint32
 // MASK bit c compiles in tile height 16 << c (16, 32, 64, 128, 256). A launch
 // must compile in every height its schedule can produce. O is the element
 // type of C; R says whether rows are grouped or gathered/scattered by index;
-// F8 selects fp8 weights with per-column scales.
-template <int MASK, Out O, Rows R, bool F8>
+// P selects the operand precisions (bf16; fp8 weights; fp8 weights and
+// activations).
+template <int MASK, Out O, Rows R, int P>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(Params p) {
   extern __shared__ __attribute__((aligned(16))) uint16_t lds_dyn[];
   __shared__ SchedLds sched;
@@ -140,17 +154,17 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(Params p) {
     switch (tl.bm) {
       case 16:
         if constexpr (MASK & 1) {
-          if (tl.bn == kWideN) tile_call<Pick<F8, Cfg16W, Cfg16FW>, O, R>(p, tl, lds);
-          else tile_call<Pick<F8, Cfg16, Cfg16F>, O, R>(p, tl, lds);
+          if (tl.bn == kWideN) tile_call<Pick<P, Cfg16W, Cfg16FW, CfgQ16W>, O, R>(p, tl, lds);
+          else tile_call<Pick<P, Cfg16, Cfg16F, CfgQ16>, O, R>(p, tl, lds);
         }
         break;
-      case 32: if constexpr (MASK & 2) tile_call<Pick<F8, Cfg32, Cfg32F>, O, R>(p, tl, lds); break;
-      case 64: if constexpr (MASK & 4) tile_call<Pick<F8, Cfg64, Cfg64F>, O, R>(p, tl, lds); break;
+      case 32: if constexpr (MASK & 2) tile_call<Pick<P, Cfg32, Cfg32F, CfgQ32>, O, R>(p, tl, lds); break;
+      case 64: if constexpr (MASK & 4) tile_call<Pick<P, Cfg64, Cfg64F, CfgQ64>, O, R>(p, tl, lds); break;
       case 128:
-        if constexpr (MASK & 8) tile_call<Pick<F8, Cfg128, Cfg128F>, O, R>(p, tl, lds);
+        if constexpr (MASK & 8) tile_call<Pick<P, Cfg128, Cfg128F, CfgQ128>, O, R>(p, tl, lds);
         break;
       default:
-        if constexpr (MASK & 16) tile_call<Pick<F8, Cfg256, Cfg256F>, O, R>(p, tl, lds);
+        if constexpr (MASK & 16) tile_call<Pick<P, Cfg256, Cfg256F, CfgQ256>, O, R>(p, tl, lds);
         break;
     }
   }
@@ -176,25 +190,26 @@ __global__ __launch_bounds__(kThreads) void tile_schedule_kernel(const int32_t *
 }
 
 // Dynamic LDS a launch needs: the largest of the heights it compiles in.
-template <int MASK, bool F8>
+template <int MASK, int P>
 constexpr int lds_bytes() {
   int m = 0;
-  if (MASK & 1) m = m > Pick<F8, Cfg16, Cfg16F>::LDS_BYTES ? m : Pick<F8, Cfg16, Cfg16F>::LDS_BYTES;
-  if (MASK & 1) m = m > Pick<F8, Cfg16W, Cfg16FW>::LDS_BYTES ? m : Pick<F8, Cfg16W, Cfg16FW>::LDS_BYTES;
-  if (MASK & 2) m = m > Pick<F8, Cfg32, Cfg32F>::LDS_BYTES ? m : Pick<F8, Cfg32, Cfg32F>::LDS_BYTES;
-  if (MASK & 4) m = m > Pick<F8, Cfg64, Cfg64F>::LDS_BYTES ? m : Pick<F8, Cfg64, Cfg64F>::LDS_BYTES;
+  if (MASK & 1) m = m > Pick<P, Cfg16, Cfg16F, CfgQ16>::LDS_BYTES ? m : Pick<P, Cfg16, Cfg16F, CfgQ16>::LDS_BYTES;
+  if (MASK & 1) m = m > Pick<P, Cfg16W, Cfg16FW, CfgQ16W>::LDS_BYTES ? m : Pick<P, Cfg16W, Cfg16FW, CfgQ16W>::LDS_BYTES;
+  if (MASK & 2) m = m > Pick<P, Cfg32, Cfg32F, CfgQ32>::LDS_BYTES ? m : Pick<P, Cfg32, Cfg32F, CfgQ32>::LDS_BYTES;
+  if (MASK & 4) m = m > Pick<P, Cfg64, Cfg64F, CfgQ64>::LDS_BYTES ? m : Pick<P, Cfg64, Cfg64F, CfgQ64>::LDS_BYTES;
   if (MASK & 8)
-    m = m > Pick<F8, Cfg128, Cfg128F>::LDS_BYTES ? m : Pick<F8, Cfg128, Cfg128F>::LDS_BYTES;
+    m = m > Pick<P, Cfg128, Cfg128F, CfgQ128>::LDS_BYTES ? m : Pick<P, Cfg128, Cfg128F, CfgQ128>::LDS_BYTES;
   if (MASK & 16)
-    m = m > Pick<F8, Cfg256, Cfg256F>::LDS_BYTES ? m : Pick<F8, Cfg256, Cfg256F>::LDS_BYTES;
+    m = m > Pick<P, Cfg256, Cfg256F, CfgQ256>::LDS_BYTES ? m : Pick<P, Cfg256, Cfg256F, CfgQ256>::LDS_BYTES;
   return m;
 }
 
 // Every launch's LDS (dynamic stages + the static schedule table) must fit
 // one CU's 160 KiB.
 constexpr int kLdsPerCu = 160 * 1024;
-static_assert(lds_bytes<31, false>() + (int)sizeof(SchedLds) <= kLdsPerCu, "LDS budget");
-static_assert(lds_bytes<31, true>() + (int)sizeof(SchedLds) <= kLdsPerCu, "LDS budget");
+static_assert(lds_bytes<31, kBf16>() + (int)sizeof(SchedLds) <= kLdsPerCu, "LDS budget");
+static_assert(lds_bytes<31, kW8>() + (int)sizeof(SchedLds) <= kLdsPerCu, "LDS budget");
+static_assert(lds_bytes<31, kW8A8>() + (int)sizeof(SchedLds) <= kLdsPerCu, "LDS budget");
 
 // Per-device, per-variant launch limits (CU count x resident workgroups).
 struct LaunchInfo {
@@ -204,21 +219,21 @@ struct LaunchInfo {
 
 constexpr int kMaxDevices = 64;
 
-template <int MASK, Out O, Rows R, bool F8>
+template <int MASK, Out O, Rows R, int P>
 static LaunchInfo launch_info(int dev) {
   static LaunchInfo cache[kMaxDevices];
   static std::once_flag once[kMaxDevices];
   std::call_once(once[dev], [dev]() {
     LaunchInfo li;
     int cus = 0, per_cu = 0;
-    const int lds = lds_bytes<MASK, F8>();
+    const int lds = lds_bytes<MASK, P>();
     li.err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (li.err == hipSuccess)
-      li.err = hipFuncSetAttribute((const void *)grouped_gemm_kernel<MASK, O, R, F8>,
+      li.err = hipFuncSetAttribute((const void *)grouped_gemm_kernel<MASK, O, R, P>,
                                    hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (li.err == hipSuccess)
       li.err = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &per_cu, (const void *)grouped_gemm_kernel<MASK, O, R, F8>, kThreads, lds);
+          &per_cu, (const void *)grouped_gemm_kernel<MASK, O, R, P>, kThreads, lds);
     if (li.err == hipSuccess) {
       if (per_cu < 1) per_cu = 1;
       li.grid = cus * per_cu;
@@ -230,16 +245,16 @@ static LaunchInfo launch_info(int dev) {
   return cache[dev];
 }
 
-template <int MASK, Out O, Rows R, bool F8>
+template <int MASK, Out O, Rows R, int P>
 static gg_status_t launch(const Params &p, long long tile_bound, hipStream_t stream) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return GG_ERR_LAUNCH;
-  const LaunchInfo li = launch_info<MASK, O, R, F8>(dev);
+  const LaunchInfo li = launch_info<MASK, O, R, P>(dev);
   if (li.err != hipSuccess) return GG_ERR_LAUNCH;
   long long g = tile_bound < li.grid ? tile_bound : li.grid;
   g = (g + kXcds - 1) / kXcds * kXcds;  // keep a multiple of the XCD count
-  constexpr int lds = lds_bytes<MASK, F8>();
-  hipLaunchKernelGGL((grouped_gemm_kernel<MASK, O, R, F8>), dim3((unsigned)g), dim3(kThreads),
+  constexpr int lds = lds_bytes<MASK, P>();
+  hipLaunchKernelGGL((grouped_gemm_kernel<MASK, O, R, P>), dim3((unsigned)g), dim3(kThreads),
                      lds, stream, p);
   return hipGetLastError() == hipSuccess ? GG_OK : GG_ERR_LAUNCH;
 }
@@ -265,9 +280,9 @@ static gg_status_t check_sizes(const int32_t *off, int E, int N, int M_cap, int 
   return GG_OK;
 }
 
-// The product with C of element type O, rows of form R and (F8) fp8 weights:
-// argument checks, then one launch.
-template <Out O, Rows R, bool F8 = false>
+// The product with C of element type O, rows of form R and operand
+// precisions P: argument checks, then one launch.
+template <Out O, Rows R, int P = kBf16>
 static gg_status_t grouped_gemm(Params p, void *stream) {
   long long bound = 0;
   gg_status_t st = check_sizes(p.off, p.E, p.N, p.M_cap, p.bm_fixed, &bound);
@@ -290,26 +305,31 @@ static gg_status_t grouped_gemm(Params p, void *stream) {
     if (p.dst_rows == nullptr || p.row_w == nullptr || p.n_dst < 0) return GG_ERR_INVALID_VALUE;
     if (!aligned(p.row_w, 4)) return GG_ERR_MISALIGNED;
   }
-  if constexpr (F8) {
+  if constexpr (P != kBf16) {
     if (p.b_scale == nullptr) return GG_ERR_INVALID_VALUE;
     if (!aligned(p.b_scale, 16)) return GG_ERR_MISALIGNED;
+  }
+  if constexpr (P == kW8A8) {
+    // 16-byte chunks of one row hold 16 fp8 values
+    if (p.a_scale == nullptr) return GG_ERR_INVALID_VALUE;
+    if (!aligned(p.a_scale, 4) || p.K % 16 != 0 || p.N % 16 != 0) return GG_ERR_MISALIGNED;
   }
   if (p.M_cap == 0 || bound == 0) return GG_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   switch (p.bm_fixed) {
-    case 16: return launch<1, O, R, F8>(p, bound, s);
-    case 32: return launch<2, O, R, F8>(p, bound, s);
-    case 64: return launch<4, O, R, F8>(p, bound, s);
-    case 128: return launch<8, O, R, F8>(p, bound, s);
-    case 256: return launch<16, O, R, F8>(p, bound, s);
-    default: return launch<31, O, R, F8>(p, bound, s);
+    case 16: return launch<1, O, R, P>(p, bound, s);
+    case 32: return launch<2, O, R, P>(p, bound, s);
+    case 64: return launch<4, O, R, P>(p, bound, s);
+    case 128: return launch<8, O, R, P>(p, bound, s);
+    case 256: return launch<16, O, R, P>(p, bound, s);
+    default: return launch<31, O, R, P>(p, bound, s);
   }
 }
 
 static Params make_params(const void *A, const void *B, const int32_t *off, void *C, int32_t E,
                           int32_t K, int32_t N, int32_t M_cap, int32_t bm) {
   return Params{static_cast<const uint16_t *>(A), static_cast<const uint16_t *>(B), off, C, E, K,
-                N, M_cap, bm, nullptr, nullptr, 0, nullptr, M_cap, nullptr};
+                N, M_cap, bm, nullptr, nullptr, 0, nullptr, nullptr, M_cap, nullptr};
 }
 
 }  // namespace gg
@@ -372,7 +392,17 @@ extern "C" gg_status_t gg_grouped_gemm_fp8w(const void *A, const void *Bq, const
                                             void *stream) {
   Params p = make_params(A, Bq, group_offsets, C, E, K, N, M_cap, bm);
   p.b_scale = b_scale;
-  return grouped_gemm<Out::F32, Rows::Grouped, true>(p, stream);
+  return grouped_gemm<Out::F32, Rows::Grouped, kW8>(p, stream);
+}
+
+extern "C" gg_status_t gg_grouped_gemm_fp8(const void *Aq, const float *a_scale, const void *Bq,
+                                           const float *b_scale, const int32_t *group_offsets,
+                                           float *C, int32_t E, int32_t K, int32_t N,
+                                           int32_t M_cap, int32_t bm, void *stream) {
+  Params p = make_params(Aq, Bq, group_offsets, C, E, K, N, M_cap, bm);
+  p.a_scale = a_scale;
+  p.b_scale = b_scale;
+  return grouped_gemm<Out::F32, Rows::Grouped, kW8A8>(p, stream);
 }
 
 extern "C" gg_status_t gg_tile_schedule(const int32_t *group_offsets, int32_t E, int32_t N,

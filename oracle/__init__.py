@@ -42,6 +42,11 @@ Contents
   fp32 scale is exact in binary64). The Pearl Pulse article ("What the 15%
   measures") mentions an FP8 scheme without details; per-output-column scales
   are the reading taken.
+* ``grouped_gemm_fp8`` / ``grouped_gemm_fp8_entries``: fp8 activations and
+  fp8 weights, C[r][n] = a_scale[r] * b_scale[e][n] * sum_k dec(Aq[r][k]) *
+  dec(Bq[e][k][n]), the same E4M3 decode, one fp32 scale per activation row
+  and per weight column (the reading taken of the article's unspecified FP8
+  scheme), the sum in binary64 (every scaled operand is exact in binary64).
 * ``round_to_bf16``: binary64 -> bfloat16 rounding to nearest, ties to even,
   written from the IEEE-754 definition of the format (8 significant bits,
   fp32's exponent range). It turns the fp64 reference into the bf16 values a
@@ -348,6 +353,44 @@ def grouped_gemm_fp8w_entries(A, Bq, scale, offsets, rows, cols):
         e = int(np.searchsorted(off, r, side="right") - 1)
         a = _bf16_to_f64(A[r])
         w = decode_e4m3(Bq[e, :, n]) * float(scale[e, n])
+        c[i] = a @ w
+        s[i] = np.abs(a) @ np.abs(w)
+    return c, s
+
+
+def grouped_gemm_fp8(Aq, a_scale, Bq, b_scale, offsets, M_cap=None):
+    """fp64 product of fp8 activations and fp8 weights. Returns (C, S), float64
+    [M_cap, N]; S[r][n] = sum_k |a_scale[r] dec(Aq[r][k]) * dec(Bq[e][k][n])
+    b_scale[e][n]|; rows outside every group are NaN."""
+    Aq = np.asarray(Aq)
+    a_scale = np.asarray(a_scale, dtype=np.float64)
+    off = np.asarray(offsets, dtype=np.int64)
+    E, K, N = Bq.shape
+    M_cap = Aq.shape[0] if M_cap is None else int(M_cap)
+    C = np.full((M_cap, N), np.nan)
+    S = np.full((M_cap, N), np.nan)
+    for e in range(E):
+        r0, r1 = int(off[e]), int(off[e + 1])
+        if r1 <= r0:
+            continue
+        a = decode_e4m3(Aq[r0:r1]) * a_scale[r0:r1, None]
+        w = _fp8_expert_weights(Bq, b_scale, e)
+        C[r0:r1] = a @ w
+        S[r0:r1] = np.abs(a) @ np.abs(w)
+    return C, S
+
+
+def grouped_gemm_fp8_entries(Aq, a_scale, Bq, b_scale, offsets, rows, cols):
+    """Selected entries of the fp8 x fp8 product, one dot product each."""
+    off = np.asarray(offsets, dtype=np.int64)
+    rows = np.asarray(rows, dtype=np.int64)
+    cols = np.asarray(cols, dtype=np.int64)
+    c = np.empty(len(rows))
+    s = np.empty(len(rows))
+    for i, (r, n) in enumerate(zip(rows, cols)):
+        e = int(np.searchsorted(off, r, side="right") - 1)
+        a = decode_e4m3(Aq[r]) * float(a_scale[r])
+        w = decode_e4m3(Bq[e, :, n]) * float(b_scale[e, n])
         c[i] = a @ w
         s[i] = np.abs(a) @ np.abs(w)
     return c, s

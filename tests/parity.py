@@ -133,3 +133,43 @@ def check_combine(y_gpu, y_ref, sw, ay, terms, what=""):
     bad = d > bound
     assert not bad.any(), "%s: %d combined elements beyond the bound (worst ratio %.3e)" % (
         what, int(bad.sum()), float(np.max(d / np.maximum(bound, 1e-300))))
+
+
+# fp8 x fp8 products on the fp8 matrix cores. An in-bounds probe of
+# v_mfma_scale_f32_16x16x128_f8f6f4 on gfx950 shows how it sums: the 128
+# products of one instruction are added in groups of 8 consecutive k (here
+# k = 8j .. 8j + 7 of a 128-deep slice), each group aligned to its largest
+# product, and a product 2^-14 of that largest or smaller is dropped while
+# 2^-12 of it is kept exactly; group sums and the accumulator then add like
+# fp32. So a group loses less than 2^-12 of its largest product for each of
+# its other 7 products, and the rest is fp32 rounding:
+#   |C_gpu - C_ref| <= 7 * 2^-12 * G + (K/8 + 3) * 2^-24 * S,
+# G = sum over groups of the largest |product| in the group, S = sum |products|
+# (both with the scales applied; the two scale multiplies are among the 3).
+FP8_GROUP = 8
+FP8_GROUP_LOSS = 7 * 2.0 ** -12
+
+
+def fp8_group_max_sum(a, w):
+    """G[r][n] = sum over aligned groups of 8 k of max_k |a[r][k] * w[k][n]|
+    (a: [m, K], w: [K, N], binary64, K a multiple of 8)."""
+    a = np.abs(np.asarray(a, dtype=np.float64))
+    w = np.abs(np.asarray(w, dtype=np.float64))
+    m, K = a.shape
+    G = np.zeros((m, w.shape[1]))
+    for k0 in range(0, K, FP8_GROUP):
+        G += np.max(a[:, k0:k0 + FP8_GROUP, None] * w[None, k0:k0 + FP8_GROUP, :], axis=1)
+    return G
+
+
+def check_fp8(c_gpu, c_ref, s_ref, g_ref, K, what=""):
+    g = np.asarray(c_gpu, dtype=np.float64)
+    r = np.asarray(c_ref, dtype=np.float64)
+    assert g.shape == r.shape, (g.shape, r.shape)
+    assert np.isfinite(g).all(), "%s: non-finite output" % what
+    bound = FP8_GROUP_LOSS * np.asarray(g_ref) + (K / FP8_GROUP + 3) * 2.0 ** -24 * np.asarray(s_ref)
+    d = np.abs(g - r)
+    bad = d > bound
+    assert not bad.any(), "%s: %d elements beyond the fp8 bound (worst ratio %.3e)" % (
+        what, int(bad.sum()), float(np.max(d / np.maximum(bound, 1e-300))))
+    return float(np.max(d / np.maximum(bound, 1e-300))) if d.size else 0.0

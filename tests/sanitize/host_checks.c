@@ -93,6 +93,24 @@ int main(void) {
                               (float *)P(128), 4, 256, 256, 29, 0, NULL),
          GG_ERR_MISALIGNED);
 
+  /* fp8 activations and weights */
+  expect("fp8: null row scales",
+         gg_grouped_gemm_fp8(P(16), NULL, P(32), (const float *)P(64), (const int32_t *)P(96),
+                             (float *)P(128), 4, 256, 256, 29, 0, NULL),
+         GG_ERR_INVALID_VALUE);
+  expect("fp8: K not a multiple of 16",
+         gg_grouped_gemm_fp8(P(16), (const float *)P(48), P(32), (const float *)P(64),
+                             (const int32_t *)P(96), (float *)P(128), 4, 264, 256, 29, 0, NULL),
+         GG_ERR_MISALIGNED);
+  expect("fp8: misaligned row scales",
+         gg_grouped_gemm_fp8(P(16), (const float *)P(50), P(32), (const float *)P(64),
+                             (const int32_t *)P(96), (float *)P(128), 4, 256, 256, 29, 0, NULL),
+         GG_ERR_MISALIGNED);
+  expect("fp8: nothing to do",
+         gg_grouped_gemm_fp8(P(16), (const float *)P(48), P(32), (const float *)P(64),
+                             (const int32_t *)P(96), (float *)P(128), 4, 256, 256, 0, 0, NULL),
+         GG_OK);
+
   /* gather / scatter */
   expect("gather: null src_rows",
          gg_grouped_gemm_bf16_gather(P(16), 10, NULL, P(32), (const int32_t *)P(64),

@@ -133,3 +133,25 @@ def test_gather_combine_host_checks(lib):
     assert call(bm=48) == 1
     assert call(n_src=2 ** 22 + 1) == 3
     assert call(M_cap=0) == 0                  # nothing to do
+
+
+def test_fp8_host_checks(lib):
+    f = lib.gg_grouped_gemm_fp8
+    names = ["Aq", "a_scale", "Bq", "b_scale", "off", "C", "E", "K", "N", "M_cap", "bm"]
+    ok = [16, 48, 32, 64, 96, 128, 4, 256, 256, 29, 0]
+
+    def call(**kw):
+        a = list(ok)
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return f(*a, None)
+    assert call(a_scale=0) == 1                # scales are required
+    assert call(b_scale=0) == 1
+    assert call(Aq=0) == 1
+    assert call(a_scale=50) == 2               # misaligned row scales
+    assert call(b_scale=72) == 2               # column scales need 16 bytes
+    assert call(K=264) == 2                    # K a multiple of 16
+    assert call(N=264) == 2                    # N a multiple of 16
+    assert call(bm=48) == 1
+    assert call(E=1025) == 3
+    assert call(M_cap=0) == 0                  # nothing to do

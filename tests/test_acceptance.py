@@ -135,3 +135,38 @@ def test_combine_check_accepts_float32_atomics_and_rejects_mistakes():
         for r in range(len(src)):
             y_bad[src[r]] += xf[src[r]] @ bf[experts[r]]
         parity.check_combine(y_bad, Y, SW, AY, terms, "unweighted")
+
+
+def test_fp8_group_bound_and_check():
+    rng = np.random.default_rng(18)
+    m, K, N = 6, 64, 5
+    a = rng.normal(size=(m, K)) * np.where(rng.random((m, K)) < 0.1, 300.0, 1.0)
+    w = rng.normal(size=(K, N))
+    # G by brute force
+    G = parity.fp8_group_max_sum(a, w)
+    for r in range(m):
+        for n in range(N):
+            want = sum(max(abs(a[r, k] * w[k, n]) for k in range(g, g + 8)) for g in range(0, K, 8))
+            assert abs(G[r, n] - want) <= 1e-12 * want
+    exact = a @ w
+    S = np.abs(a) @ np.abs(w)
+    # emulate the observed hardware sum: in each group of 8, products at or
+    # below 2^-14 of the group's largest are dropped
+    hw = np.zeros((m, N))
+    for r in range(m):
+        for n in range(N):
+            for g in range(0, K, 8):
+                p = a[r, g:g + 8] * w[g:g + 8, n]
+                big = np.abs(p).max()
+                hw[r, n] += p[np.abs(p) > 2.0 ** -14 * big].sum()
+    parity.check_fp8(exact, exact, S, G, K, "exact")
+    parity.check_fp8(hw, exact, S, G, K, "group-truncated")
+    with pytest.raises(AssertionError):
+        parity.check_fp8(exact * 1.01, exact, S, G, K, "scaled by 1.01")
+    # without outliers, losing one whole product is far outside the bound
+    a2 = rng.normal(size=(m, K))
+    e2 = a2 @ w
+    S2, G2 = np.abs(a2) @ np.abs(w), parity.fp8_group_max_sum(a2, w)
+    parity.check_fp8(e2, e2, S2, G2, K, "exact, no outliers")
+    with pytest.raises(AssertionError):
+        parity.check_fp8(e2 - a2[:, 5:6] @ w[5:6, :], e2, S2, G2, K, "one k dropped")

@@ -582,3 +582,77 @@ def test_combine_linear_in_weights_and_start_values():
     Y4, _, _, _ = oracle.grouped_gemm_combine(X, src, w.B, w.offsets, dst, g, 16)
     C, _ = oracle.grouped_gemm_indexed(X, src, w.B, w.offsets, dst_rows=None, M_cap=len(src))
     assert np.allclose(Y4[src[0]], Y1[src[0]] - g[0] * C[0], rtol=1e-12, atol=1e-12)
+
+
+# ---- fp8 activations and fp8 weights ---------------------------------------------
+
+def test_fp8_brute_force_integers():
+    # small integers are exact E4M3 codes; scales are powers of two, so every
+    # product and sum is exact and the scalar loop must agree bit for bit
+    rng = np.random.default_rng(36)
+    E, K, N = 3, 9, 5
+    sizes = [2, 0, 4]
+    off = wl.offsets_from_sizes(sizes)
+    av = rng.integers(-3, 4, size=(6, K))
+    qv = rng.integers(-3, 4, size=(E, K, N))
+    Aq, Bq = _int_codes(av), _int_codes(qv)
+    a_scale = np.ldexp(1.0, rng.integers(-2, 3, size=6)).astype(np.float32)
+    b_scale = np.ldexp(1.0, rng.integers(-3, 4, size=(E, N))).astype(np.float32)
+    c, s = oracle.grouped_gemm_fp8(Aq, a_scale, Bq, b_scale, off)
+    for e in range(E):
+        for r in range(off[e], off[e + 1]):
+            for n in range(N):
+                acc = 0.0
+                for k in range(K):
+                    acc += float(av[r, k]) * float(qv[e, k, n])
+                assert c[r, n] == acc * float(a_scale[r]) * float(b_scale[e, n])
+                assert s[r, n] >= abs(c[r, n])
+
+
+def test_fp8_unit_activation_scale_reduces_to_fp8_weight_product():
+    # every E4M3 value is a bf16 value: with unit activation scales the fp8 x
+    # fp8 product is the fp8-weight product of the decoded activations
+    rng = np.random.default_rng(37)
+    E, K, N = 4, 64, 24
+    sizes = [5, 0, 9, 3]
+    off = wl.offsets_from_sizes(sizes)
+    Aq = rng.integers(0, 256, size=(17, K)).astype(np.uint8)
+    Aq[(Aq & 0x7F) == 0x7F] = 0x38  # no NaN codes
+    Bq = rng.integers(0, 256, size=(E, K, N)).astype(np.uint8)
+    Bq[(Bq & 0x7F) == 0x7F] = 0x40
+    b_scale = rng.uniform(0.01, 2.0, size=(E, N)).astype(np.float32)
+    c1, s1 = oracle.grouped_gemm_fp8(Aq, np.ones(17, np.float32), Bq, b_scale, off)
+    A_bf16 = wl.f32_to_bf16_bits(oracle.decode_e4m3(Aq).astype(np.float32))
+    c2, s2 = oracle.grouped_gemm_fp8w(A_bf16, Bq, b_scale, off)
+    m = int(off[-1])
+    assert np.allclose(c1[:m], c2[:m], rtol=1e-12, atol=1e-12 * np.abs(s1[:m]).max())
+    assert np.allclose(s1[:m], s2[:m], rtol=1e-12)
+    # the activation scale multiplies whole rows; a power of two is exact
+    a_scale = np.ldexp(1.0, rng.integers(-4, 5, size=17)).astype(np.float32)
+    c3, _ = oracle.grouped_gemm_fp8(Aq, a_scale, Bq, b_scale, off)
+    assert np.array_equal(c3[:m], c1[:m] * a_scale[:m, None].astype(np.float64))
+
+
+def test_fp8_entries_match_full_product():
+    rng = np.random.default_rng(38)
+    w = wl.make_workload(E=3, K=48, N=32, sizes=[7, 0, 12], seed=39)
+    Aq, a_scale = wl.fp8_activations(w)
+    Bq, b_scale = wl.fp8_weights(w)
+    C, S = oracle.grouped_gemm_fp8(Aq, a_scale, Bq, b_scale, w.offsets)
+    rows = rng.integers(0, w.M_tot, size=40)
+    cols = rng.integers(0, w.N, size=40)
+    c, s = oracle.grouped_gemm_fp8_entries(Aq, a_scale, Bq, b_scale, w.offsets, rows, cols)
+    assert np.allclose(c, C[rows, cols], rtol=1e-13, atol=1e-15)
+    assert np.allclose(s, S[rows, cols], rtol=1e-13)
+
+
+def test_fp8_activation_recipe_is_close_to_bf16_activations():
+    # E4M3 keeps 4 significant bits: each activation is within 2^-4 of its
+    # value relative to the row scale's range, and the scale is max|row|/448
+    w = wl.make_workload(E=2, K=96, N=16, sizes=[9, 4], seed=40)
+    Aq, a_scale = wl.fp8_activations(w)
+    a = wl.bf16_bits_to_f32(w.A).astype(np.float64)
+    back = oracle.decode_e4m3(Aq) * a_scale[:, None]
+    rowmax = np.abs(a).max(axis=1, keepdims=True)
+    assert np.allclose(a_scale, (np.abs(a).max(axis=1) / 448).astype(np.float32))
+    assert (np.abs(back - a) <= 2.0 ** -4 * np.maximum(np.abs(a), rowmax * 2.0 ** -6) + 1e-30).all()

@@ -780,6 +780,122 @@ def test_fp8w_decode_shape_sampled(gg):
     assert (d <= parity.ELEM * s).all()
 
 
+# ---- fp8 activations and fp8 weights (fp8 matrix cores) ---------------------------
+
+def _q8_run(gg, Aq, a_scale, Bq, b_scale, offsets, M_cap, N, bm):
+    dev = torch.device("cuda:0")
+    C = torch.full((M_cap, N), float("nan"), dtype=torch.float32, device=dev)
+    gg.grouped_gemm_fp8(torch.from_numpy(Aq).to(dev), torch.from_numpy(a_scale).to(dev),
+                        torch.from_numpy(Bq).to(dev), torch.from_numpy(b_scale).to(dev),
+                        torch.from_numpy(offsets).to(dev), out=C, bm=bm)
+    torch.cuda.synchronize()
+    return C.cpu().numpy()
+
+
+def _q8_group_max(Aq, a_scale, Bq, b_scale, offsets, M_cap):
+    """The fp8 bound's G term, expert by expert (rows outside groups: 0)."""
+    off = np.asarray(offsets, dtype=np.int64)
+    G = np.zeros((M_cap, Bq.shape[2]))
+    for e in range(Bq.shape[0]):
+        r0, r1 = int(off[e]), int(off[e + 1])
+        if r1 > r0:
+            a = oracle.decode_e4m3(Aq[r0:r1]) * a_scale[r0:r1, None].astype(np.float64)
+            wt = oracle.decode_e4m3(Bq[e]) * b_scale[e][None, :].astype(np.float64)
+            G[r0:r1] = parity.fp8_group_max_sum(a, wt)
+    return G
+
+
+def _q8_check(got, Aq, a_scale, Bq, b_scale, offsets, M_cap, what):
+    ref, s = oracle.grouped_gemm_fp8(Aq, a_scale, Bq, b_scale, offsets, M_cap=M_cap)
+    G = _q8_group_max(Aq, a_scale, Bq, b_scale, offsets, M_cap)
+    m = int(np.asarray(offsets)[-1])
+    worst = parity.check_fp8(got[:m], ref[:m], s[:m], G[:m], Aq.shape[1], what)
+    _say("  %s: worst error / bound %.3e" % (what, worst))
+    assert np.isnan(got[m:]).all(), "%s: rows past the last group were written" % what
+
+
+def _q8_compare(gg, w, bm, what):
+    Aq, a_scale = wl.fp8_activations(w)
+    Bq, b_scale = wl.fp8_weights(w)
+    _say("case fp8 %s E=%d K=%d N=%d M_tot=%d bm=%d" % (what, w.E, w.K, w.N, w.M_tot, bm))
+    got = _q8_run(gg, Aq, a_scale, Bq, b_scale, w.offsets, w.M_cap, w.N, bm)
+    _q8_check(got, Aq, a_scale, Bq, b_scale, w.offsets, w.M_cap, what)
+
+
+@pytest.mark.parametrize("bm", BMS)
+def test_fp8_tiny(gg, bm):
+    _q8_compare(gg, wl.make_workload("tiny"), bm, "tiny")
+
+
+@pytest.mark.parametrize("bm", BMS)
+def test_fp8_ragged_wide(gg, bm):
+    # N = 784: three full 256-column tiles and a 16-column one; K = 208: one
+    # full 128-deep slice and a partial one
+    w = wl.make_workload(E=4, K=208, N=784, sizes=[300, 0, 45, 517], seed=27, M_cap=870)
+    _q8_compare(gg, w, bm, "fp8 ragged-wide")
+
+
+@pytest.mark.parametrize("bm", [0, 16, 64, 256])
+def test_fp8_integer_codes_exact(gg, bm):
+    # small-integer codes and power-of-two scales: every product, sum and
+    # scaling is exact, so the result must equal the oracle bit for bit
+    rng = np.random.default_rng(42)
+    sizes = [5, 0, 40, 129, 16]
+    off = wl.offsets_from_sizes(sizes)
+    E, K, N = 5, 256, 272
+    M = int(off[-1])
+    table = {0: 0x00, 1: 0x38, 2: 0x40, 3: 0x44}
+    def codes(v):
+        return (np.vectorize(table.get)(np.abs(v)) | ((v < 0) << 7)).astype(np.uint8)
+    Aq = codes(rng.integers(-3, 4, size=(M, K)))
+    Bq = codes(rng.integers(-3, 4, size=(E, K, N)))
+    a_scale = np.ldexp(1.0, rng.integers(-3, 4, size=M)).astype(np.float32)
+    b_scale = np.ldexp(1.0, rng.integers(-3, 4, size=(E, N))).astype(np.float32)
+    _say("case fp8 int-exact bm=%d" % bm)
+    got = _q8_run(gg, Aq, a_scale, Bq, b_scale, off, M, N, bm)
+    ref, _ = oracle.grouped_gemm_fp8(Aq, a_scale, Bq, b_scale, off)
+    assert np.array_equal(got, ref)
+
+
+def test_fp8_all_codes(gg):
+    # every finite E4M3 code appears in both operands (NaN codes excluded)
+    rng = np.random.default_rng(43)
+    finite = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    sizes = [17, 3, 0, 44]
+    off = wl.offsets_from_sizes(sizes)
+    E, K, N = 4, 384, 256
+    M = int(off[-1])
+    Aq = rng.choice(finite, size=(M, K))
+    Bq = rng.choice(finite, size=(E, K, N))
+    Aq[0, :254] = finite
+    Bq[0, :254, 0] = finite
+    a_scale = rng.uniform(0.5, 2.0, size=M).astype(np.float32)
+    b_scale = rng.uniform(0.5, 2.0, size=(E, N)).astype(np.float32)
+    _say("case fp8 all codes")
+    got = _q8_run(gg, Aq, a_scale, Bq, b_scale, off, M, N, 0)
+    _q8_check(got, Aq, a_scale, Bq, b_scale, off, M, "fp8 all codes")
+
+
+@pytest.mark.parametrize("name", ["decode", "uniform16k"])
+def test_fp8_full_size_sampled(gg, name):
+    w = _full(name)
+    Aq, a_scale = wl.fp8_activations(w)
+    Bq, b_scale = wl.fp8_weights(w)
+    _say("case fp8 full %s" % name)
+    got = _q8_run(gg, Aq, a_scale, Bq, b_scale, w.offsets, w.M_cap, w.N, 0)
+    assert np.isfinite(got[: w.M_tot]).all()
+    rows, cols = _samples(w, np.random.default_rng(11))
+    c, s = oracle.grouped_gemm_fp8_entries(Aq, a_scale, Bq, b_scale, w.offsets, rows, cols)
+    G = np.empty(len(rows))
+    for i, (r, n) in enumerate(zip(rows, cols)):
+        e = int(np.searchsorted(w.offsets, r, side="right") - 1)
+        a = oracle.decode_e4m3(Aq[r:r + 1]) * float(a_scale[r])
+        wt = oracle.decode_e4m3(Bq[e][:, n:n + 1]) * float(b_scale[e, n])
+        G[i] = parity.fp8_group_max_sum(a, wt)[0, 0]
+    worst = parity.check_fp8(got[rows, cols], c, s, G, w.K, name + " fp8 sampled")
+    _say("  %s fp8 sampled: worst error / bound %.3e" % (name, worst))
+
+
 # ---- several tiles per workgroup (the pipelined tile loop) -----------------------------
 
 @pytest.mark.parametrize("bm", BMS)

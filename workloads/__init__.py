@@ -256,6 +256,21 @@ def f32_to_e4m3_bits(x: np.ndarray) -> np.ndarray:
     return code.astype(np.uint8)
 
 
+def fp8_activations(w: "Workload"):
+    """fp8 E4M3 codes and per-row fp32 scales for w.A (rows past the last group
+    included).
+
+    scale[r] = max_k |A[r, k]| / 448 (1 for an all-zero row), computed in
+    float32; codes = E4M3 rounding of A[r, k] / scale[r] (float32 division).
+    Returns (codes uint8 [M_cap, K], scale float32 [M_cap]).
+    """
+    a = bf16_bits_to_f32(w.A)
+    scale = (np.abs(a).max(axis=1) / np.float32(448.0)).astype(np.float32)
+    scale[scale == 0] = 1.0
+    codes = f32_to_e4m3_bits(a / scale[:, None])
+    return codes, scale
+
+
 def fp8_weights(w: "Workload"):
     """fp8 E4M3 codes and per-(expert, column) fp32 scales for w.B.
 

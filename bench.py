@@ -201,7 +201,7 @@ def main():
     if args.weights == "fp8":
         # fp8 E4M3 weights with per-(expert, column) fp32 scales, quantized
         # from the bf16 weights on the host (input recipe, untimed)
-        if args.out != "fp32" or args.gather:
+        if (args.out != "fp32" and args.acts == "bf16") or args.gather:
             raise SystemExit("--weights fp8 times the fp32-output grouped-row entry point")
         q_np, sc_np = wl.fp8_weights(w)
         Bq = torch.from_numpy(q_np).to(dev)
@@ -210,6 +210,8 @@ def main():
     if args.acts == "fp8":
         if args.weights != "fp8":
             raise SystemExit("--acts fp8 needs --weights fp8")
+        if args.out not in ("fp32", "bf16") or args.gather:
+            raise SystemExit("--acts fp8 times the grouped-row fp32 or bf16-output entry points")
         aq_np, as_np = wl.fp8_activations(w)
         Aq = torch.from_numpy(aq_np).to(dev)
         As = torch.from_numpy(as_np).to(dev)

@@ -246,6 +246,18 @@ gg_status_t gg_grouped_gemm_fp8(const void *Aq, const float *a_scale, const void
                                 void *stream);
 
 /*
+ * gg_grouped_gemm_fp8_bf16out -- gg_grouped_gemm_fp8 with bf16 output: C is
+ * bf16 [M_cap][N], 16-byte aligned, each element the fp32 result of
+ * gg_grouped_gemm_fp8 (scales applied) rounded once to the nearest bf16
+ * (ties to even). Every other argument and rule is that of
+ * gg_grouped_gemm_fp8.
+ */
+gg_status_t gg_grouped_gemm_fp8_bf16out(const void *Aq, const float *a_scale, const void *Bq,
+                                        const float *b_scale, const int32_t *group_offsets,
+                                        void *C, int32_t E, int32_t K, int32_t N, int32_t M_cap,
+                                        int32_t bm, void *stream);
+
+/*
  * gg_tile_schedule -- the flat tile list the product kernel consumes,
  * written out (worklog section 2: one descriptor per output tile of one
  * expert, expert-major order, tiles stopping at expert boundaries, empty

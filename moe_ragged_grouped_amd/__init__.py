@@ -33,7 +33,8 @@ def tile_widths(heights, sizes):
 MAX_EXPERTS = 1024
 SYMBOLS = ("gg_grouped_gemm_bf16", "gg_grouped_gemm_bf16_bf16out", "gg_grouped_gemm_bf16_swiglu",
            "gg_grouped_gemm_bf16_gather", "gg_grouped_gemm_bf16_gather_combine",
-           "gg_grouped_gemm_fp8w", "gg_grouped_gemm_fp8", "gg_tile_schedule", "gg_status_string")
+           "gg_grouped_gemm_fp8w", "gg_grouped_gemm_fp8", "gg_grouped_gemm_fp8_bf16out",
+           "gg_tile_schedule", "gg_status_string")
 
 _lib = None
 
@@ -71,6 +72,9 @@ def load_library():
         lib.gg_grouped_gemm_fp8w.restype = ctypes.c_int
         lib.gg_grouped_gemm_fp8.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
         lib.gg_grouped_gemm_fp8.restype = ctypes.c_int
+        lib.gg_grouped_gemm_fp8_bf16out.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
+                                                    i32, vp]
+        lib.gg_grouped_gemm_fp8_bf16out.restype = ctypes.c_int
         lib.gg_tile_schedule.argtypes = [vp, i32, i32, i32, i32, vp, vp, i32, vp]
         lib.gg_tile_schedule.restype = ctypes.c_int
         lib.gg_status_string.argtypes = [ctypes.c_int]
@@ -283,12 +287,15 @@ def grouped_gemm_fp8w(A, Bq, b_scale, offsets, out=None, bm: int = 0, stream=Non
     return out
 
 
-def grouped_gemm_fp8(Aq, a_scale, Bq, b_scale, offsets, out=None, bm: int = 0, stream=None):
+def grouped_gemm_fp8(Aq, a_scale, Bq, b_scale, offsets, out=None, bm: int = 0, stream=None,
+                     out_dtype=None):
     """C = (a_scale * dec(Aq)) @ (dec(Bq[e]) * b_scale[e]) per expert, fp8 matrix cores.
 
     Aq: uint8 [M_cap, K] E4M3 codes; a_scale: fp32 [M_cap]; Bq: uint8
     [E, K, N] E4M3 codes; b_scale: fp32 [E, N]; offsets int32 [E+1]; out:
-    optional fp32 [M_cap, N]. K and N must be multiples of 16.
+    optional fp32 or bf16 [M_cap, N] (out_dtype when out is not given,
+    default fp32; bf16 is the fp32 result rounded to nearest even). K and N
+    must be multiples of 16.
     """
     import torch
     lib = load_library()
@@ -309,13 +316,18 @@ def grouped_gemm_fp8(Aq, a_scale, Bq, b_scale, offsets, out=None, bm: int = 0, s
             or offsets.shape[0] != E + 1):
         raise ValueError("shape mismatch")
     if out is None:
-        out = torch.empty((M_cap, N), dtype=torch.float32, device=Aq.device)
-    elif out.dtype != torch.float32 or tuple(out.shape) != (M_cap, N) or not out.is_contiguous():
-        raise ValueError("out must be a contiguous fp32 [M_cap, N] tensor")
-    st = lib.gg_grouped_gemm_fp8(Aq.data_ptr(), a_scale.data_ptr(), Bq.data_ptr(),
-                                 b_scale.data_ptr(), offsets.data_ptr(), out.data_ptr(), E, K, N,
-                                 M_cap, int(bm), _stream_handle(Aq.device, stream))
-    _check(st, "gg_grouped_gemm_fp8")
+        dt = torch.float32 if out_dtype is None else out_dtype
+        if dt not in (torch.float32, torch.bfloat16):
+            raise TypeError("out_dtype must be torch.float32 or torch.bfloat16")
+        out = torch.empty((M_cap, N), dtype=dt, device=Aq.device)
+    elif (out.dtype not in (torch.float32, torch.bfloat16) or tuple(out.shape) != (M_cap, N)
+          or not out.is_contiguous() or (out_dtype is not None and out.dtype != out_dtype)):
+        raise ValueError("out must be a contiguous fp32 or bf16 [M_cap, N] tensor")
+    fn = lib.gg_grouped_gemm_fp8 if out.dtype == torch.float32 else lib.gg_grouped_gemm_fp8_bf16out
+    st = fn(Aq.data_ptr(), a_scale.data_ptr(), Bq.data_ptr(), b_scale.data_ptr(),
+            offsets.data_ptr(), out.data_ptr(), E, K, N, M_cap, int(bm),
+            _stream_handle(Aq.device, stream))
+    _check(st, fn.__name__)
     return out
 
 

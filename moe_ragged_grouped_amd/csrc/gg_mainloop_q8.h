@@ -174,10 +174,11 @@ __device__ __forceinline__ void mma_stage_q8(f32x4 (&acc)[C::NI][C::MI], const l
   }
 }
 
-// Full K loop and epilogue of one fp8 tile (grouped rows, fp32 C). The loop
-// is the bf16 one: A one slice and B BD slices ahead in registers, two LDS
-// stages, one barrier per slice, a branch-free unrolled steady state.
-template <class C>
+// Full K loop and epilogue of one fp8 tile (grouped rows; C in fp32, or
+// rounded once to bf16 when O is Out::BF16). The loop is the bf16 one: A one
+// slice and B BD slices ahead in registers, two LDS stages, one barrier per
+// slice, a branch-free unrolled steady state.
+template <class C, Out O>
 __device__ __forceinline__ void run_tile_q8(const TileArgs &t, lds_u16 *lds_base) {
   lds_u8 *const lds = (lds_u8 *)lds_base;
   lds_u8 *const As0 = lds;                       // stage s: As0 + s * A_STAGE
@@ -240,8 +241,13 @@ __device__ __forceinline__ void run_tile_q8(const TileArgs &t, lds_u16 *lds_base
 #pragma unroll
       for (int ni = 0; ni < C::NI; ++ni) {
         const int n = wn0 + ni * 16 + 4 * g;
-        if (n < t.ncols)
-          st_g16((float *)t.C + (size_t)m * t.N + n, acc[ni][mi] * sa * ld_g16f(t.scale + n));
+        if (n < t.ncols) {
+          const f32x4 v = acc[ni][mi] * sa * ld_g16f(t.scale + n);
+          if constexpr (O == Out::F32)
+            st_g16((float *)t.C + (size_t)m * t.N + n, v);
+          else
+            st_g8_bf16((uint16_t *)t.C + (size_t)m * t.N + n, v);
+        }
       }
     }
   }

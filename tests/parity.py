@@ -173,3 +173,17 @@ def check_fp8(c_gpu, c_ref, s_ref, g_ref, K, what=""):
     assert not bad.any(), "%s: %d elements beyond the fp8 bound (worst ratio %.3e)" % (
         what, int(bad.sum()), float(np.max(d / np.maximum(bound, 1e-300))))
     return float(np.max(d / np.maximum(bound, 1e-300))) if d.size else 0.0
+
+
+def check_fp8_bf16(c_gpu, c_ref, s_ref, g_ref, K, what=""):
+    """bf16 output of the fp8 x fp8 product: the fp32 result meets check_fp8's
+    bound and is rounded once to nearest, so the bf16 value lies between the
+    bf16 roundings of ref -/+ that bound."""
+    import oracle
+    g = np.asarray(c_gpu, dtype=np.float64)
+    r = np.asarray(c_ref, dtype=np.float64)
+    assert g.shape == r.shape, (g.shape, r.shape)
+    assert np.isfinite(g).all(), "%s: non-finite output" % what
+    bound = FP8_GROUP_LOSS * np.asarray(g_ref) + (K / FP8_GROUP + 3) * 2.0 ** -24 * np.asarray(s_ref)
+    bad = (g < oracle.round_to_bf16(r - bound)) | (g > oracle.round_to_bf16(r + bound))
+    assert not bad.any(), "%s: %d bf16 elements outside their bracket" % (what, int(bad.sum()))

@@ -135,8 +135,9 @@ def test_gather_combine_host_checks(lib):
     assert call(M_cap=0) == 0                  # nothing to do
 
 
-def test_fp8_host_checks(lib):
-    f = lib.gg_grouped_gemm_fp8
+@pytest.mark.parametrize("fn", ["gg_grouped_gemm_fp8", "gg_grouped_gemm_fp8_bf16out"])
+def test_fp8_host_checks(lib, fn):
+    f = getattr(lib, fn)
     names = ["Aq", "a_scale", "Bq", "b_scale", "off", "C", "E", "K", "N", "M_cap", "bm"]
     ok = [16, 48, 32, 64, 96, 128, 4, 256, 256, 29, 0]
 

@@ -876,6 +876,28 @@ def test_fp8_all_codes(gg):
     _q8_check(got, Aq, a_scale, Bq, b_scale, off, M, "fp8 all codes")
 
 
+@pytest.mark.parametrize("bm", [0, 16, 256])
+def test_fp8_bf16_out(gg, bm):
+    # against the oracle (bracketed bf16 bound), and bit for bit the fp32
+    # entry point's result rounded to bf16 by torch
+    w = wl.make_workload(E=4, K=208, N=784, sizes=[300, 0, 45, 517], seed=27, M_cap=870)
+    Aq, a_scale = wl.fp8_activations(w)
+    Bq, b_scale = wl.fp8_weights(w)
+    dev = torch.device("cuda:0")
+    args = [torch.from_numpy(x).to(dev) for x in (Aq, a_scale, Bq, b_scale, w.offsets)]
+    _say("case fp8 bf16-out bm=%d" % bm)
+    c16 = torch.full((w.M_cap, w.N), float("nan"), dtype=torch.bfloat16, device=dev)
+    gg.grouped_gemm_fp8(*args, out=c16, bm=bm)
+    c32 = gg.grouped_gemm_fp8(*args, bm=bm)
+    torch.cuda.synchronize()
+    m = w.M_tot
+    assert torch.equal(c32[:m].cpu().to(torch.bfloat16).view(torch.int16), c16[:m].cpu().view(torch.int16))
+    assert torch.isnan(c16[m:].float()).all()
+    ref, s = oracle.grouped_gemm_fp8(Aq, a_scale, Bq, b_scale, w.offsets, M_cap=w.M_cap)
+    G = _q8_group_max(Aq, a_scale, Bq, b_scale, w.offsets, w.M_cap)
+    parity.check_fp8_bf16(c16[:m].float().cpu().numpy(), ref[:m], s[:m], G[:m], w.K, "fp8 bf16-out")
+
+
 @pytest.mark.parametrize("name", ["decode", "uniform16k"])
 def test_fp8_full_size_sampled(gg, name):
     w = _full(name)

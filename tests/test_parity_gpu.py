@@ -961,6 +961,46 @@ def test_graph_capture_replays(gg):
         torch.cuda.synchronize()
 
 
+@pytest.mark.parametrize("entry", ["swiglu", "fp8", "gather"])
+def test_graph_capture_other_entry_points(gg, entry):
+    # each entry point enqueues one kernel and allocates nothing, so it can be
+    # captured; every replay reproduces the eager result
+    w = wl.make_workload(E=6, K=320, N=400, sizes=[0, 1, 17, 130, 0, 300], seed=21, M_cap=470)
+    dev = torch.device("cuda:0")
+    A, B, off = _dev(w)
+    if entry == "swiglu":
+        run = lambda out: gg.grouped_gemm_swiglu(A, B, off, out=out, bm=0)
+        out = torch.empty((w.M_cap, w.N // 2), dtype=torch.bfloat16, device=dev)
+    elif entry == "fp8":
+        Aq, a_scale = wl.fp8_activations(w)
+        Bq, b_scale = wl.fp8_weights(w)
+        q = [torch.from_numpy(x).to(dev) for x in (Aq, a_scale, Bq, b_scale)]
+        run = lambda out: gg.grouped_gemm_fp8(q[0], q[1], q[2], q[3], off, out=out, bm=0)
+        out = torch.empty((w.M_cap, w.N), dtype=torch.float32, device=dev)
+    else:
+        perm = torch.from_numpy(np.random.default_rng(3).permutation(w.M_cap).astype(np.int32)).to(dev)
+        run = lambda out: gg.grouped_gemm_gather(A, perm, B, off, dst_rows=perm, out=out, bm=0)
+        out = torch.empty((w.M_cap, w.N), dtype=torch.float32, device=dev)
+    eager = run(torch.full_like(out, float("nan"))).clone()
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    _say("case graph capture %s" % entry)
+    with torch.cuda.graph(g, stream=s):
+        run(out)
+    torch.cuda.synchronize()
+    for i in range(3):
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16) if out.dtype == torch.bfloat16 else out.nan_to_num(7.0),
+                           eager.view(torch.int16) if eager.dtype == torch.bfloat16 else eager.nan_to_num(7.0)), "replay %d" % i
+        torch.randn(1 << 20, device=dev).sum()
+        torch.cuda.synchronize()
+
+
 def test_concurrent_streams(gg):
     # the library keeps no mutable state per call: launches of different
     # problems and entry points on two streams, queued without a sync between

@@ -104,7 +104,8 @@ gg_status_t gg_grouped_gemm_bf16_bf16out(const void *A, const void *B,
  * gg_grouped_gemm_bf16_swiglu -- the gate and up projections with the SwiGLU
  * activation applied in the epilogue.
  *
- * The Pearl Pulse article ("What the 15% measures") benchmarks the kernel on
+ * The Pearl Pulse page "Pearl's grouped GEMM kernel for MoE models,
+ * explained" (section "What the 15% measures") benchmarks the kernel on
  * the gate and up projections of MoE models; the activation between them
  * and the next projection is silu(gate) * up. Here B holds both projections
  * with their columns interleaved, so the product's two columns of one output
@@ -196,7 +197,7 @@ gg_status_t gg_grouped_gemm_bf16_gather_combine(const void *X, int32_t n_src,
 
 /*
  * gg_grouped_gemm_fp8w -- the product with fp8 weights and per-column scales
- * (the Pearl Pulse article, "What the 15% measures", notes that its kernel
+ * (the Pearl Pulse page, "What the 15% measures", notes that its kernel
  * ships with an FP8 scheme; the scheme below is this library's reading).
  *
  *   C[r][n] = scale[e][n] * sum_k A[r][k] * dec(Bq[e][k][n])   for r in group e

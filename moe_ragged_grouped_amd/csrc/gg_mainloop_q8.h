@@ -4,8 +4,9 @@
 //
 //   C[r][n] = a_scale[r] * b_scale[e][n] * sum_k dec(Aq[r][k]) * dec(Bq[e][k][n])
 //
-// The Pearl Pulse article ("What the 15% measures") says the kernel ships
-// with an FP8 scheme and gives no details; one fp32 scale per activation row
+// The Pearl Pulse page "Pearl's grouped GEMM kernel for MoE models,
+// explained" (section "What the 15% measures") says the kernel ships with an
+// FP8 scheme and gives no details; one fp32 scale per activation row
 // and one per weight column is the reading taken. The tile walk, the tile
 // heights and widths, the buffer-resource zero fill and the epilogue layout
 // are those of the bf16 kernel (gg_mainloop.h); what changes:

@@ -39,9 +39,10 @@ Contents
   the fp8-weight product C[r][n] = scale[e][n] * sum_k a[r][k] * dec(q[e][k][n])
   with the OCP E4M3 decode written from the format's definition, and the sum
   in binary64 (numpy float64 matmul per expert; the decoded weight times its
-  fp32 scale is exact in binary64). The Pearl Pulse article ("What the 15%
-  measures") mentions an FP8 scheme without details; per-output-column scales
-  are the reading taken.
+  fp32 scale is exact in binary64). The Pearl Pulse page "Pearl's grouped
+  GEMM kernel for MoE models, explained" (section "What the 15% measures")
+  mentions an FP8 scheme without details; per-output-column scales are the
+  reading taken.
 * ``grouped_gemm_fp8`` / ``grouped_gemm_fp8_entries``: fp8 activations and
   fp8 weights, C[r][n] = a_scale[r] * b_scale[e][n] * sum_k dec(Aq[r][k]) *
   dec(Bq[e][k][n]), the same E4M3 decode, one fp32 scale per activation row
@@ -63,7 +64,7 @@ Contents
   error budget carried through the weights), |Y0| + sum_r |w[r] * C[r]| and
   the number of terms.
 * ``silu`` / ``swiglu_pairs``: the SwiGLU activation between the gate and up
-  projections the Pearl Pulse article benchmarks ("What the 15% measures"):
+  projections the Pearl Pulse page benchmarks ("What the 15% measures"):
   silu(x) = x * sigmoid(x) = x / (1 + e^-x), and H[:, j] = silu(C[:, 2j]) *
   C[:, 2j+1] for a product whose columns interleave gate (even) and up (odd)
   -- the column layout of the fused entry point, written out directly.

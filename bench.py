@@ -62,12 +62,18 @@ DESCRIPTIONS = {
 
 
 def kernel_source_hash():
+    """Hash of the kernel sources with comments and blank space taken out, so
+    that a change to a comment does not mark the measured counters stale."""
+    import re
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "moe_ragged_grouped_amd", "csrc")
     for fn in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, fn), "rb") as f:
-            h.update(fn.encode())
-            h.update(f.read())
+        with open(os.path.join(csrc, fn), encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(fn.encode())
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -213,6 +213,45 @@ def test_malformed_offsets_stay_in_bounds(gg):
     parity.check(Cw.cpu().numpy(), ref, s, "clamped")
 
 
+@pytest.mark.parametrize("entry", ["bf16out", "swiglu", "fp8w", "fp8", "gather", "combine"])
+def test_malformed_offsets_other_entry_points(gg, entry):
+    # every entry point shares the clamped schedule: malformed offsets never
+    # move a read or a write outside the caller's buffers (guard rows after
+    # the output stay NaN, guard rows after the inputs are never needed)
+    w = wl.make_workload(E=4, K=64, N=128, sizes=[10, 10, 10, 10], seed=26)
+    dev = torch.device("cuda:0")
+    A, B, _ = _dev(w)
+    guard = 8
+    Bq, b_scale = wl.fp8_weights(w)
+    Aq, a_scale = wl.fp8_activations(w)
+    q = [torch.from_numpy(x).to(dev) for x in (Aq, a_scale, Bq, b_scale)]
+    idx = torch.arange(w.M_cap, dtype=torch.int32, device=dev)
+    ones = torch.ones(w.M_cap, dtype=torch.float32, device=dev)
+    for bad in ([-5, 10, 5, 30, 40], [0, 10, 20, 30, 99], [0, 50, 20, 30, 40]):
+        _say("case malformed %s %s" % (entry, bad))
+        off = torch.tensor(bad, dtype=torch.int32, device=dev)
+        cols = w.N // 2 if entry == "swiglu" else w.N
+        dt = torch.bfloat16 if entry in ("bf16out", "swiglu") else torch.float32
+        big = torch.full((w.M_cap + guard, cols), float("nan"), dtype=dt, device=dev)
+        out = big[: w.M_cap]
+        if entry == "bf16out":
+            gg.grouped_gemm(A, B, off, out=out, bm=0)
+        elif entry == "swiglu":
+            gg.grouped_gemm_swiglu(A, B, off, out=out, bm=0)
+        elif entry == "fp8w":
+            gg.grouped_gemm_fp8w(A, q[2], q[3], off, out=out, bm=0)
+        elif entry == "fp8":
+            gg.grouped_gemm_fp8(q[0], q[1], q[2], q[3], off, out=out, bm=0)
+        elif entry == "gather":
+            gg.grouped_gemm_gather(A, idx, B, off, dst_rows=idx, out=out, bm=0)
+        else:
+            big.zero_()
+            gg.grouped_gemm_gather_combine(A, idx, B, off, idx, ones, out=out, bm=0)
+        torch.cuda.synchronize()
+        tail = big[w.M_cap:].float().cpu().numpy()
+        assert (np.isnan(tail).all() if entry != "combine" else (tail == 0).all()), entry
+
+
 # ---- full-size workloads, sampled ------------------------------------------------
 
 FULL = ["decode", "uniform16k", "skew16k", "skew2k_wide"]

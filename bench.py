@@ -166,6 +166,8 @@ def main():
                     help="time the gather + weighted-combine entry point (fp32 atomic adds "
                          "into the token rows; with --gather's top-1 permutation)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra-timings", action="store_true",
+                    help="skip the graph-captured and cold-cache timings")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (for counter calibration)")
     args = ap.parse_args()
@@ -328,6 +330,49 @@ def main():
     schedule = {"tiles": int(n_tiles), "m_tiles": int(len(first)), "m_tiles_by_height": heights,
                 "eta": round(float(first[:, 2].sum()) / max(1.0, float(first[:, 4].sum())), 4)}
 
+    # Two more timings of the same launch, outside the timed region above:
+    #  graph: launches captured in a HIP graph (no host launch cost, as the
+    #    worklog and the Pearl Pulse page time their kernels), median per launch;
+    #  cold: each launch timed alone after a 512 MB write has pushed the
+    #    inputs out of the L2s and the 256 MB Infinity Cache, median.
+    extra = {}
+    if not args.no_extra_timings:
+        n_rep = 20
+        gs = torch.cuda.Stream(dev)
+        gs.wait_stream(stream)
+        with torch.cuda.stream(gs):
+            step()  # settle allocations on the capture stream
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=gs):
+            for _ in range(n_rep):
+                step()
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(5):
+            g0 = torch.cuda.Event(enable_timing=True)
+            g1 = torch.cuda.Event(enable_timing=True)
+            g0.record(stream)
+            graph.replay()
+            g1.record(stream)
+            torch.cuda.synchronize()
+            times.append(g0.elapsed_time(g1) * 1e3 / n_rep)
+        extra["graph_median_us"] = round(float(np.median(times)), 2)
+        del graph
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        cold = []
+        for i in range(n_rep):
+            flush.fill_(i & 0xFF)
+            c0 = torch.cuda.Event(enable_timing=True)
+            c1 = torch.cuda.Event(enable_timing=True)
+            c0.record(stream)
+            step()
+            c1.record(stream)
+            torch.cuda.synchronize()
+            cold.append(c0.elapsed_time(c1) * 1e3)
+        extra["cold_median_us"] = round(float(np.median(cold)), 2)
+        del flush
+
     cpu = None
     if not args.no_cpu_baseline:
         print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
@@ -361,6 +406,7 @@ def main():
         "mfma_frac": round(tflops_launch / mfma_peak, 4),
         "roofline": roof,
         "schedule": schedule,
+        "timings": extra,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

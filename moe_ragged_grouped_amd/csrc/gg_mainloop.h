@@ -338,6 +338,90 @@ __device__ __forceinline__ void combine_epilogue(const TileArgs &t, f32x4 (&acc)
   __syncthreads();
 }
 
+// The K loop every operand type shares. Slices of A and B are loaded AD and
+// BD slices ahead of their use. Tiles that share A rows or B columns run side
+// by side and request the same lines at about the same time, so most loads
+// wait for HBM, not L2. The steady-state loop (every slice but the last) is
+// unrolled so that each staging buffer and each LDS stage has a fixed name,
+// and its body is free of branches: slices past K are still "loaded" (all
+// lanes out of range, so zeros and no memory traffic). The compiler's
+// in-order vmcnt accounting then stores slice s+1 while the loads of later
+// slices stay in flight.
+//
+// Ops supplies, for a compile-time staging slot J: load_a(J, kt) and
+// load_b(J, kt) (slice kt, global -> registers), store_a(J, stage) and
+// store_b(J, stage) (registers -> LDS stage), and mma(stage). Ends with a
+// workgroup barrier, so the next tile may refill the stages at once.
+template <int J>
+using Slot = std::integral_constant<int, J>;
+
+template <int AD, int BD, int NS, class Ops>
+__device__ __forceinline__ void k_loop(int KT, Ops &ops) {
+  static_for<(AD > BD ? AD : BD)>([&](auto jc) {
+    constexpr int j = decltype(jc)::value;
+    if constexpr (j < AD) ops.load_a(jc, j);
+    if constexpr (j < BD) ops.load_b(jc, j);
+  });
+  ops.store_a(Slot<0>{}, 0);
+  ops.store_b(Slot<0>{}, 0);
+  __syncthreads();
+
+  // one steady-state step: slice kt (kt % U == j) from its stage, slice kt + 1
+  // into the other
+  auto step = [&](auto jc, int kt) {
+    constexpr int j = decltype(jc)::value;
+    constexpr int cur = j % NS, nxt = (j + 1) % NS;
+    ops.load_a(Slot<j % AD>{}, kt + AD);
+    ops.load_b(Slot<j % BD>{}, kt + BD);
+    // keep the loads ahead of the matrix work (the scheduler would otherwise
+    // sink them next to their LDS stores and expose their latency)
+    __builtin_amdgcn_sched_barrier(0);
+    ops.mma(cur);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (NS == 1) __syncthreads();  // every wave is done reading the stage
+    ops.store_a(Slot<(j + 1) % AD>{}, nxt);
+    ops.store_b(Slot<(j + 1) % BD>{}, nxt);
+    __syncthreads();
+  };
+  // unroll factor: a multiple of AD, BD and 2
+  constexpr int U = lcm(lcm(AD, BD), 2);
+  int kt0 = 0;
+  for (; kt0 + U <= KT - 1; kt0 += U)
+    static_for<U>([&](auto jc) { step(jc, kt0 + decltype(jc)::value); });
+  static_for<U - 1>([&](auto jc) {
+    if (kt0 + decltype(jc)::value < KT - 1) step(jc, kt0 + decltype(jc)::value);
+  });
+  // the last slice sits in stage (KT - 1) % NS
+  ops.mma((KT - 1) % NS);
+  __syncthreads();
+}
+
+// The K-loop operations of the bf16-activation tiles (bf16 or fp8 weights).
+template <class C>
+struct KOpsBf16 {
+  Loads<C> &L;
+  Staging<C> &st;
+  const TileArgs &t;
+  lds_u16 *As0, *Bs0;
+  f32x4 (*acc)[C::NI][C::MI];
+  int wm0, wn0, lane;
+  template <int J>
+  __device__ __forceinline__ void load_a(Slot<J>, int kt) { gg::load_a<C>(st.a[J], L, t, kt * C::BK); }
+  template <int J>
+  __device__ __forceinline__ void load_b(Slot<J>, int kt) { gg::load_b<C>(st.b[J], L, t, kt * C::BK); }
+  template <int J>
+  __device__ __forceinline__ void store_a(Slot<J>, int stage) {
+    gg::store_a<C>(st.a[J], As0 + stage * C::A_STAGE, t.tid);
+  }
+  template <int J>
+  __device__ __forceinline__ void store_b(Slot<J>, int stage) {
+    gg::store_b<C>(st.b[J], Bs0 + stage * C::B_STAGE, t.tid);
+  }
+  __device__ __forceinline__ void mma(int stage) {
+    mma_stage<C>(*acc, As0 + stage * C::A_STAGE, Bs0 + stage * C::B_STAGE, wm0, wn0, lane);
+  }
+};
+
 // Full K loop and epilogue for one tile. lds must hold C::LDS_BYTES. Ends with
 // a workgroup barrier, so the next tile may refill the stages at once. O is
 // what the epilogue writes: fp32 C (the accumulators as they are), bf16 C
@@ -359,57 +443,12 @@ __device__ __forceinline__ void run_tile(const TileArgs &t, lds_u16 *lds) {
 #pragma unroll
     for (int mi = 0; mi < C::MI; ++mi) acc[ni][mi] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Slices of A and B are loaded AD and BD slices ahead of their use. Tiles
-  // that share A rows or B columns run side by side and request the same
-  // lines at about the same time, so most loads wait for HBM, not L2. The
-  // steady-state loop (every slice but the last) is unrolled so that each
-  // staging buffer and each LDS stage has a fixed name, and its body is free
-  // of branches: slices past K are still "loaded" (all lanes out of range,
-  // so zeros and no memory traffic). The compiler's in-order vmcnt
-  // accounting then stores slice s+1 while the loads of later slices stay in
-  // flight.
   const int KT = cdiv(t.K, C::BK);
   Loads<C> L;
   init_loads<C, R>(L, t);
   Staging<C> st;
-  static_for<(C::AD > C::BD ? C::AD : C::BD)>([&](auto jc) {
-    constexpr int j = decltype(jc)::value;
-    if constexpr (j < C::AD) load_a<C>(st.a[j], L, t, j * C::BK);
-    if constexpr (j < C::BD) load_b<C>(st.b[j], L, t, j * C::BK);
-  });
-  store_a<C>(st.a[0], As0, t.tid);
-  store_b<C>(st.b[0], Bs0, t.tid);
-  __syncthreads();
-
-  // one steady-state step: slice kt (kt % U == j) from its stage, slice kt + 1
-  // into the other
-  auto step = [&](auto jc, int kt) {
-    constexpr int j = decltype(jc)::value;
-    constexpr int cur = j % C::NS, nxt = (j + 1) % C::NS;
-    load_a<C>(st.a[j % C::AD], L, t, (kt + C::AD) * C::BK);
-    load_b<C>(st.b[j % C::BD], L, t, (kt + C::BD) * C::BK);
-    // keep the loads ahead of the matrix work (the scheduler would otherwise
-    // sink them next to their LDS stores and expose their latency)
-    __builtin_amdgcn_sched_barrier(0);
-    mma_stage<C>(acc, As0 + cur * C::A_STAGE, Bs0 + cur * C::B_STAGE, wm0, wn0, lane);
-    __builtin_amdgcn_sched_barrier(0);
-    if constexpr (C::NS == 1) __syncthreads();  // every wave is done reading the stage
-    store_a<C>(st.a[(j + 1) % C::AD], As0 + nxt * C::A_STAGE, t.tid);
-    store_b<C>(st.b[(j + 1) % C::BD], Bs0 + nxt * C::B_STAGE, t.tid);
-    __syncthreads();
-  };
-  // unroll factor: a multiple of AD, BD and 2
-  constexpr int U = lcm(lcm(C::AD, C::BD), 2);
-  int kt0 = 0;
-  for (; kt0 + U <= KT - 1; kt0 += U)
-    static_for<U>([&](auto jc) { step(jc, kt0 + decltype(jc)::value); });
-  static_for<U - 1>([&](auto jc) {
-    if (kt0 + decltype(jc)::value < KT - 1) step(jc, kt0 + decltype(jc)::value);
-  });
-  // the last slice sits in stage (KT - 1) % NS
-  const int last = (KT - 1) % C::NS;
-  mma_stage<C>(acc, As0 + last * C::A_STAGE, Bs0 + last * C::B_STAGE, wm0, wn0, lane);
-  __syncthreads();
+  KOpsBf16<C> ops{L, st, t, As0, Bs0, &acc, wm0, wn0, lane};
+  k_loop<C::AD, C::BD, C::NS>(KT, ops);
 
   // epilogue: lane holds C[m][n..n+3] for m = s, n = 4g within each 16x16 block
   const int g = lane / 16, s = lane % 16;

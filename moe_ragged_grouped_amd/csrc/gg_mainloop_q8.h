@@ -175,10 +175,36 @@ __device__ __forceinline__ void mma_stage_q8(f32x4 (&acc)[C::NI][C::MI], const l
   }
 }
 
+// The K-loop operations of the fp8 x fp8 tiles (see k_loop in gg_mainloop.h).
+template <class C>
+struct KOpsQ8 {
+  LoadsQ8<C> &L;
+  StagingQ8<C> &st;
+  const TileArgs &t;
+  lds_u8 *As0, *Bs0;
+  f32x4 (*acc)[C::NI][C::MI];
+  int wm0, wn0, lane;
+  template <int J>
+  __device__ __forceinline__ void load_a(Slot<J>, int kt) { load_a_q8<C>(st.a[J], L, t, kt * C::BK); }
+  template <int J>
+  __device__ __forceinline__ void load_b(Slot<J>, int kt) { load_b_q8<C>(st.b[J], L, t, kt * C::BK); }
+  template <int J>
+  __device__ __forceinline__ void store_a(Slot<J>, int stage) {
+    store_a_q8<C>(st.a[J], As0 + stage * C::A_STAGE, t.tid);
+  }
+  template <int J>
+  __device__ __forceinline__ void store_b(Slot<J>, int stage) {
+    store_b_q8<C>(st.b[J], Bs0 + stage * C::B_STAGE, t.tid);
+  }
+  __device__ __forceinline__ void mma(int stage) {
+    mma_stage_q8<C>(*acc, As0 + stage * C::A_STAGE, Bs0 + stage * C::B_STAGE, wm0, wn0, lane);
+  }
+};
+
 // Full K loop and epilogue of one fp8 tile (grouped rows; C in fp32, or
-// rounded once to bf16 when O is Out::BF16). The loop is the bf16 one: A one
-// slice and B BD slices ahead in registers, two LDS stages, one barrier per
-// slice, a branch-free unrolled steady state.
+// rounded once to bf16 when O is Out::BF16). The loop is the shared k_loop:
+// A one slice and B BD slices ahead in registers, two LDS stages, one barrier
+// per slice, a branch-free unrolled steady state.
 template <class C, Out O>
 __device__ __forceinline__ void run_tile_q8(const TileArgs &t, lds_u16 *lds_base) {
   lds_u8 *const lds = (lds_u8 *)lds_base;
@@ -199,37 +225,8 @@ __device__ __forceinline__ void run_tile_q8(const TileArgs &t, lds_u16 *lds_base
   LoadsQ8<C> L;
   init_loads_q8<C>(L, t);
   StagingQ8<C> st;
-  static_for<(C::AD > C::BD ? C::AD : C::BD)>([&](auto jc) {
-    constexpr int j = decltype(jc)::value;
-    if constexpr (j < C::AD) load_a_q8<C>(st.a[j], L, t, j * C::BK);
-    if constexpr (j < C::BD) load_b_q8<C>(st.b[j], L, t, j * C::BK);
-  });
-  store_a_q8<C>(st.a[0], As0, t.tid);
-  store_b_q8<C>(st.b[0], Bs0, t.tid);
-  __syncthreads();
-
-  auto step = [&](auto jc, int kt) {
-    constexpr int j = decltype(jc)::value;
-    constexpr int cur = j % 2, nxt = (j + 1) % 2;
-    load_a_q8<C>(st.a[j % C::AD], L, t, (kt + C::AD) * C::BK);
-    load_b_q8<C>(st.b[j % C::BD], L, t, (kt + C::BD) * C::BK);
-    __builtin_amdgcn_sched_barrier(0);
-    mma_stage_q8<C>(acc, As0 + cur * C::A_STAGE, Bs0 + cur * C::B_STAGE, wm0, wn0, lane);
-    __builtin_amdgcn_sched_barrier(0);
-    store_a_q8<C>(st.a[(j + 1) % C::AD], As0 + nxt * C::A_STAGE, t.tid);
-    store_b_q8<C>(st.b[(j + 1) % C::BD], Bs0 + nxt * C::B_STAGE, t.tid);
-    __syncthreads();
-  };
-  constexpr int U = lcm(lcm(C::AD, C::BD), 2);
-  int kt0 = 0;
-  for (; kt0 + U <= KT - 1; kt0 += U)
-    static_for<U>([&](auto jc) { step(jc, kt0 + decltype(jc)::value); });
-  static_for<U - 1>([&](auto jc) {
-    if (kt0 + decltype(jc)::value < KT - 1) step(jc, kt0 + decltype(jc)::value);
-  });
-  const int last = (KT - 1) % 2;
-  mma_stage_q8<C>(acc, As0 + last * C::A_STAGE, Bs0 + last * C::B_STAGE, wm0, wn0, lane);
-  __syncthreads();
+  KOpsQ8<C> ops{L, st, t, As0, Bs0, &acc, wm0, wn0, lane};
+  k_loop<C::AD, C::BD, 2>(KT, ops);
 
   // epilogue: lane holds C[m][n..n+3] for m = s, n = 4g within each 16x16
   // block, times the row's activation scale and the columns' weight scales

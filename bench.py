@@ -218,8 +218,8 @@ def main():
     if args.acts == "fp8":
         if args.weights != "fp8":
             raise SystemExit("--acts fp8 needs --weights fp8")
-        if args.out not in ("fp32", "bf16") or args.gather:
-            raise SystemExit("--acts fp8 times the grouped-row fp32 or bf16-output entry points")
+        if args.gather:
+            raise SystemExit("--acts fp8 times the grouped-row entry points")
         aq_np, as_np = wl.fp8_activations(w)
         Aq = torch.from_numpy(aq_np).to(dev)
         As = torch.from_numpy(as_np).to(dev)
@@ -244,7 +244,9 @@ def main():
             C.zero_()
 
     def step():
-        if args.acts == "fp8":
+        if args.acts == "fp8" and args.out == "swiglu":
+            gg.grouped_gemm_fp8_swiglu(Aq, As, Bq, Bs, off, out=C, bm=args.bm)
+        elif args.acts == "fp8":
             gg.grouped_gemm_fp8(Aq, As, Bq, Bs, off, out=C, bm=args.bm)
         elif args.weights == "fp8":
             gg.grouped_gemm_fp8w(A, Bq, Bs, off, out=C, bm=args.bm)

@@ -116,9 +116,12 @@ gg_status_t gg_grouped_gemm_bf16_bf16out(const void *A, const void *B,
  *   H   bf16 [M_cap][N/2], row-major, 16-byte aligned:
  *       H[r][j] = silu(C[r][2j]) * C[r][2j+1], silu(x) = x / (1 + e^-x),
  *       where C is the fp32 product gg_grouped_gemm_bf16 computes for the
- *       same inputs. The activation is evaluated in fp32 (an accurate expf
- *       and an IEEE division) and rounded once to the nearest bf16 (ties to
- *       even). Rows at or past off[E] are not written.
+ *       same inputs. The activation is evaluated in fp32 as
+ *       x * rcp(1 + 2^(-x log2 e)) with the hardware exp2 and reciprocal,
+ *       within (|gate| + 3.5) * 2^-23 of the exact value relative to first
+ *       order (-0 where e^-gate overflows, for gate below about -88.7), and
+ *       rounded once to the nearest bf16 (ties to even). Rows at or past
+ *       off[E] are not written.
  * A, group_offsets, E, K, N, M_cap, bm, the stream, the status codes and
  * the conditions for them are those of gg_grouped_gemm_bf16 (N a multiple
  * of 8, so I is a multiple of 4).
@@ -257,6 +260,20 @@ gg_status_t gg_grouped_gemm_fp8_bf16out(const void *Aq, const float *a_scale, co
                                         const float *b_scale, const int32_t *group_offsets,
                                         void *C, int32_t E, int32_t K, int32_t N, int32_t M_cap,
                                         int32_t bm, void *stream);
+
+/*
+ * gg_grouped_gemm_fp8_swiglu -- gg_grouped_gemm_fp8 for the gate and up
+ * projections with the SwiGLU of gg_grouped_gemm_bf16_swiglu in the
+ * epilogue: Bq's columns interleave gate (even) and up (odd), and
+ *   H[r][j] = silu(C[r][2j]) * C[r][2j+1]   (bf16 [M_cap][N/2], 16-byte aligned)
+ * where C is the scaled fp32 result gg_grouped_gemm_fp8 computes. The
+ * activation and its rounding are those of gg_grouped_gemm_bf16_swiglu;
+ * every other argument and rule is that of gg_grouped_gemm_fp8.
+ */
+gg_status_t gg_grouped_gemm_fp8_swiglu(const void *Aq, const float *a_scale, const void *Bq,
+                                       const float *b_scale, const int32_t *group_offsets,
+                                       void *H, int32_t E, int32_t K, int32_t N, int32_t M_cap,
+                                       int32_t bm, void *stream);
 
 /*
  * gg_tile_schedule -- the flat tile list the product kernel consumes,

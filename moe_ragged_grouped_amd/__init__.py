@@ -14,7 +14,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["grouped_gemm", "grouped_gemm_swiglu", "grouped_gemm_gather", "grouped_gemm_gather_combine", "grouped_gemm_fp8w", "grouped_gemm_fp8", "tile_schedule", "library_path", "load_library", "GroupedGemmError",
+__all__ = ["grouped_gemm", "grouped_gemm_swiglu", "grouped_gemm_gather", "grouped_gemm_gather_combine", "grouped_gemm_fp8w", "grouped_gemm_fp8", "grouped_gemm_fp8_swiglu", "tile_schedule", "library_path", "load_library", "GroupedGemmError",
            "BM_CHOICES", "TILE_N", "TILE_N_WIDE", "tile_widths", "MAX_EXPERTS", "SYMBOLS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -34,7 +34,7 @@ MAX_EXPERTS = 1024
 SYMBOLS = ("gg_grouped_gemm_bf16", "gg_grouped_gemm_bf16_bf16out", "gg_grouped_gemm_bf16_swiglu",
            "gg_grouped_gemm_bf16_gather", "gg_grouped_gemm_bf16_gather_combine",
            "gg_grouped_gemm_fp8w", "gg_grouped_gemm_fp8", "gg_grouped_gemm_fp8_bf16out",
-           "gg_tile_schedule", "gg_status_string")
+           "gg_grouped_gemm_fp8_swiglu", "gg_tile_schedule", "gg_status_string")
 
 _lib = None
 
@@ -75,6 +75,9 @@ def load_library():
         lib.gg_grouped_gemm_fp8_bf16out.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
                                                     i32, vp]
         lib.gg_grouped_gemm_fp8_bf16out.restype = ctypes.c_int
+        lib.gg_grouped_gemm_fp8_swiglu.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
+                                                   i32, vp]
+        lib.gg_grouped_gemm_fp8_swiglu.restype = ctypes.c_int
         lib.gg_tile_schedule.argtypes = [vp, i32, i32, i32, i32, vp, vp, i32, vp]
         lib.gg_tile_schedule.restype = ctypes.c_int
         lib.gg_status_string.argtypes = [ctypes.c_int]
@@ -328,6 +331,41 @@ def grouped_gemm_fp8(Aq, a_scale, Bq, b_scale, offsets, out=None, bm: int = 0, s
             offsets.data_ptr(), out.data_ptr(), E, K, N, M_cap, int(bm),
             _stream_handle(Aq.device, stream))
     _check(st, fn.__name__)
+    return out
+
+
+def grouped_gemm_fp8_swiglu(Aq, a_scale, Bq, b_scale, offsets, out=None, bm: int = 0,
+                            stream=None):
+    """H[r, j] = silu(C[r, 2j]) * C[r, 2j+1] for C = the fp8 x fp8 product.
+
+    Arguments as in grouped_gemm_fp8; Bq's columns interleave gate (even) and
+    up (odd); out: optional bf16 [M_cap, N // 2].
+    """
+    import torch
+    lib = load_library()
+    if Aq.dtype != torch.uint8 or Bq.dtype != torch.uint8:
+        raise TypeError("Aq and Bq must be uint8 E4M3 codes")
+    if a_scale.dtype != torch.float32 or b_scale.dtype != torch.float32:
+        raise TypeError("a_scale and b_scale must be float32")
+    if offsets.dtype != torch.int32:
+        raise TypeError("offsets must be int32")
+    tensors = [Aq, a_scale, Bq, b_scale, offsets]
+    if not all(t.is_cuda and t.is_contiguous() for t in tensors):
+        raise ValueError("all tensors must be contiguous device tensors")
+    E, K, N = Bq.shape
+    M_cap = Aq.shape[0]
+    if (Aq.dim() != 2 or Aq.shape[1] != K or tuple(a_scale.shape) != (M_cap,)
+            or tuple(b_scale.shape) != (E, N) or tuple(offsets.shape) != (E + 1,)):
+        raise ValueError("shape mismatch")
+    if out is None:
+        out = torch.empty((M_cap, N // 2), dtype=torch.bfloat16, device=Aq.device)
+    elif (out.dtype != torch.bfloat16 or tuple(out.shape) != (M_cap, N // 2)
+          or not out.is_contiguous()):
+        raise ValueError("out must be a contiguous bf16 [M_cap, N // 2] tensor")
+    st = lib.gg_grouped_gemm_fp8_swiglu(Aq.data_ptr(), a_scale.data_ptr(), Bq.data_ptr(),
+                                        b_scale.data_ptr(), offsets.data_ptr(), out.data_ptr(),
+                                        E, K, N, M_cap, int(bm), _stream_handle(Aq.device, stream))
+    _check(st, "gg_grouped_gemm_fp8_swiglu")
     return out
 
 

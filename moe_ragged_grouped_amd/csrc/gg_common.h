@@ -121,12 +121,19 @@ __device__ __forceinline__ void st_g8_bf16(uint16_t *p, f32x4 v) {
 
 // SwiGLU of one lane's four columns, taken as two (gate, up) pairs:
 // v = (g0, u0, g1, u1) -> silu(g0) * u0, silu(g1) * u1 with
-// silu(x) = x / (1 + e^-x), evaluated in fp32 (accurate expf, IEEE division;
-// e^-x overflows to infinity for very negative x, giving -0), each rounded
-// once to bf16 (ties to even) and stored as one 4-byte global store.
+// silu(x) = x / (1 + e^-x) = x * rcp(1 + 2^(-x log2 e)), evaluated in fp32
+// with the hardware exp2 and reciprocal (v_exp_f32, v_rcp_f32, each within
+// one ulp). Rounding -x log2 e moves the exponent by up to |x| log2(e) 2^-23,
+// so the result is within about (|x| + 3.5) 2^-23 of silu(x) * u relative; e^-x
+// overflows to infinity for x below about -88.7, giving -0 where the exact
+// value is below 3e-37. Each result is rounded once to bf16 (ties to even)
+// and the pair stored as one 4-byte global store.
 typedef __attribute__((ext_vector_type(2))) float f32x2;
 typedef __attribute__((address_space(1))) bf16x2 gbl_bf16x2;
-__device__ __forceinline__ float silu(float x) { return x / (1.0f + expf(-x)); }
+__device__ __forceinline__ float silu(float x) {
+  constexpr float kLog2e = 1.4426950408889634f;
+  return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-x * kLog2e));
+}
 __device__ __forceinline__ void st_g4_swiglu_bf16(uint16_t *p, f32x4 v) {
   const f32x2 h = {silu(v.x) * v.y, silu(v.z) * v.w};
   *(gbl_bf16x2 *)p = __builtin_convertvector(h, bf16x2);

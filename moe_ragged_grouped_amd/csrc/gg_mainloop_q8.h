@@ -201,8 +201,9 @@ struct KOpsQ8 {
   }
 };
 
-// Full K loop and epilogue of one fp8 tile (grouped rows; C in fp32, or
-// rounded once to bf16 when O is Out::BF16). The loop is the shared k_loop:
+// Full K loop and epilogue of one fp8 tile (grouped rows; C in fp32, rounded
+// once to bf16 when O is Out::BF16, or the bf16 SwiGLU of interleaved (gate,
+// up) column pairs when O is Out::SwiGluBF16). The loop is the shared k_loop:
 // A one slice and B BD slices ahead in registers, two LDS stages, one barrier
 // per slice, a branch-free unrolled steady state.
 template <class C, Out O>
@@ -243,8 +244,10 @@ __device__ __forceinline__ void run_tile_q8(const TileArgs &t, lds_u16 *lds_base
           const f32x4 v = acc[ni][mi] * sa * ld_g16f(t.scale + n);
           if constexpr (O == Out::F32)
             st_g16((float *)t.C + (size_t)m * t.N + n, v);
-          else
+          else if constexpr (O == Out::BF16)
             st_g8_bf16((uint16_t *)t.C + (size_t)m * t.N + n, v);
+          else  // SwiGLU of the (gate, up) pairs (n, n+1), (n+2, n+3), scales applied
+            st_g4_swiglu_bf16((uint16_t *)t.C + (size_t)m * (t.N / 2) + n / 2, v);
         }
       }
     }

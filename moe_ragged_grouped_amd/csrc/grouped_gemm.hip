@@ -118,8 +118,8 @@ __device__ __forceinline__ void tile_body(const Params &p, int row0, int rows, i
   asm volatile("" : "+v"(tid));
   a.tid = tid;
   if constexpr (Cfg::Q8) {
-    static_assert((O == Out::F32 || O == Out::BF16) && R == Rows::Grouped,
-                  "fp8 activations: grouped rows, fp32 or bf16 C");
+    static_assert(O != Out::AddF32 && R == Rows::Grouped,
+                  "fp8 activations: grouped rows; fp32, bf16 or SwiGLU output");
     run_tile_q8<Cfg, O>(a, lds);
   } else {
     run_tile<Cfg, O, R>(a, lds);
@@ -415,6 +415,17 @@ extern "C" gg_status_t gg_grouped_gemm_fp8_bf16out(const void *Aq, const float *
   p.a_scale = a_scale;
   p.b_scale = b_scale;
   return grouped_gemm<Out::BF16, Rows::Grouped, kW8A8>(p, stream);
+}
+
+extern "C" gg_status_t gg_grouped_gemm_fp8_swiglu(const void *Aq, const float *a_scale,
+                                                  const void *Bq, const float *b_scale,
+                                                  const int32_t *group_offsets, void *H,
+                                                  int32_t E, int32_t K, int32_t N, int32_t M_cap,
+                                                  int32_t bm, void *stream) {
+  Params p = make_params(Aq, Bq, group_offsets, H, E, K, N, M_cap, bm);
+  p.a_scale = a_scale;
+  p.b_scale = b_scale;
+  return grouped_gemm<Out::SwiGluBF16, Rows::Grouped, kW8A8>(p, stream);
 }
 
 extern "C" gg_status_t gg_tile_schedule(const int32_t *group_offsets, int32_t E, int32_t N,

@@ -68,14 +68,32 @@ def check_bf16(c_gpu, c_ref, s_ref, what=""):
 # silu falls on (-inf, x*] and rises on [x*, inf), x* = -1 - W(1/e), so over
 # an interval it is largest at an end and smallest at an end or at x*; the
 # product with the u interval is bounded by its four corners. The fp32
-# evaluation (expf within a few ulp, the sum, the IEEE division and the
-# product each within half an ulp) adds at most 2^-20 of the value, while
-# inputs stay well inside fp32's range (|g| below a few hundred), plus, where
-# e^-g overflows or the result underflows, an absolute error below
-# 2^-100 * |u| (the exact |silu(g)| is then below 3e-37). The bf16 output must
-# lie between the bf16 roundings of the widened bounds.
-SWIGLU_EVAL_REL = 2.0 ** -20
+# evaluation x * rcp(1 + 2^(-x log2 e)) with the hardware exp2 and
+# reciprocal (each within one ulp, 2^-23 relative), three roundings of 2^-24
+# (the sum, the product with x, the product with u), and the rounding of
+# -x log2 e (log2 e itself rounded too, 2^-23 in all), which moves the
+# exponent by at most |x| log2(e) 2^-23 and so the value by |x| 2^-23: in
+# all at most (|g| + 3.5) 2^-23 relative to first order; the check allows
+# (|g| + 4) 2^-22. Where e^-g overflows (g below about -88.7) the kernel
+# returns -0 while the exact |silu(g)| is below 3e-37: an absolute
+# 2^-100 * |u| covers it. The bf16 output must lie between the bf16
+# roundings of the widened bounds.
 SWIGLU_EVAL_ABS = 2.0 ** -100
+
+
+def swiglu_eval_rel(g_abs):
+    """Relative bound on the kernel's fp32 evaluation of silu(g) * u."""
+    return (np.asarray(g_abs, dtype=np.float64) + 4.0) * 2.0 ** -22
+
+
+def swiglu_eval_slack(c32, h64):
+    """Allowed |kernel - exact| for silu(g) * u evaluated from fp32 g, u.
+
+    c32 holds the interleaved fp32 (gate, up) columns the kernel activates;
+    h64 their exact SwiGLU."""
+    c = np.asarray(c32, dtype=np.float64)
+    return swiglu_eval_rel(np.abs(c[..., 0::2])) * np.abs(h64) + \
+        SWIGLU_EVAL_ABS * np.maximum(1.0, np.abs(c[..., 1::2]))
 
 
 def silu_range(lo, hi):
@@ -90,24 +108,27 @@ def silu_range(lo, hi):
     return smin, np.maximum(a, b)
 
 
-def swiglu_bounds(c_ref, s_ref):
-    """[lo, hi] for the fp32 SwiGLU of a product meeting the fp32 bar."""
+def swiglu_bounds(c_ref, s_ref, err=None):
+    """[lo, hi] for the fp32 SwiGLU of a product meeting the fp32 bar, or
+    within err (per product element) of c_ref when err is given."""
     c = np.asarray(c_ref, dtype=np.float64)
     s = np.asarray(s_ref, dtype=np.float64)
+    e = ELEM * s if err is None else np.asarray(err, dtype=np.float64)
     g, u = c[..., 0::2], c[..., 1::2]
-    eg, eu = ELEM * s[..., 0::2], ELEM * s[..., 1::2]
+    eg, eu = e[..., 0::2], e[..., 1::2]
     sl, sh = silu_range(g - eg, g + eg)
     corners = np.stack([sl * (u - eu), sl * (u + eu), sh * (u - eu), sh * (u + eu)])
     lo, hi = corners.min(axis=0), corners.max(axis=0)
-    slack = SWIGLU_EVAL_REL * np.maximum(np.abs(lo), np.abs(hi)) + \
+    g_abs = np.maximum(np.abs(g - eg), np.abs(g + eg))
+    slack = swiglu_eval_rel(g_abs) * np.maximum(np.abs(lo), np.abs(hi)) + \
         SWIGLU_EVAL_ABS * np.maximum(1.0, np.abs(u) + eu)
     return lo - slack, hi + slack
 
 
-def check_swiglu_bf16(h_gpu, c_ref, s_ref, what=""):
+def check_swiglu_bf16(h_gpu, c_ref, s_ref, what="", err=None):
     import oracle
     h = np.asarray(h_gpu, dtype=np.float64)
-    lo, hi = swiglu_bounds(c_ref, s_ref)
+    lo, hi = swiglu_bounds(c_ref, s_ref, err)
     assert h.shape == lo.shape, (h.shape, lo.shape)
     assert np.isfinite(h).all(), "%s: non-finite output" % what
     bad = (h < oracle.round_to_bf16(lo)) | (h > oracle.round_to_bf16(hi))
@@ -187,3 +208,8 @@ def check_fp8_bf16(c_gpu, c_ref, s_ref, g_ref, K, what=""):
     bound = FP8_GROUP_LOSS * np.asarray(g_ref) + (K / FP8_GROUP + 3) * 2.0 ** -24 * np.asarray(s_ref)
     bad = (g < oracle.round_to_bf16(r - bound)) | (g > oracle.round_to_bf16(r + bound))
     assert not bad.any(), "%s: %d bf16 elements outside their bracket" % (what, int(bad.sum()))
+
+
+def fp8_bound(s_ref, g_ref, K):
+    """check_fp8's bound, per element."""
+    return FP8_GROUP_LOSS * np.asarray(g_ref) + (K / FP8_GROUP + 3) * 2.0 ** -24 * np.asarray(s_ref)

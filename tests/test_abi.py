@@ -135,7 +135,8 @@ def test_gather_combine_host_checks(lib):
     assert call(M_cap=0) == 0                  # nothing to do
 
 
-@pytest.mark.parametrize("fn", ["gg_grouped_gemm_fp8", "gg_grouped_gemm_fp8_bf16out"])
+@pytest.mark.parametrize("fn", ["gg_grouped_gemm_fp8", "gg_grouped_gemm_fp8_bf16out",
+                                "gg_grouped_gemm_fp8_swiglu"])
 def test_fp8_host_checks(lib, fn):
     f = getattr(lib, fn)
     names = ["Aq", "a_scale", "Bq", "b_scale", "off", "C", "E", "K", "N", "M_cap", "bm"]

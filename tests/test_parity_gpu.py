@@ -444,8 +444,9 @@ def test_swiglu_is_activated_fp32_product(gg, bm):
     h = gg.grouped_gemm_swiglu(A, B, off, bm=bm)
     torch.cuda.synchronize()
     m = w.M_tot
-    h64 = oracle.swiglu_pairs(c32[:m].cpu().numpy().astype(np.float64))
-    slack = parity.SWIGLU_EVAL_REL * np.abs(h64) + parity.SWIGLU_EVAL_ABS
+    c64 = c32[:m].cpu().numpy().astype(np.float64)
+    h64 = oracle.swiglu_pairs(c64)
+    slack = parity.swiglu_eval_slack(c64, h64)
     got = h[:m].float().cpu().numpy().astype(np.float64)
     assert (got >= oracle.round_to_bf16(h64 - slack)).all()
     assert (got <= oracle.round_to_bf16(h64 + slack)).all()
@@ -935,6 +936,36 @@ def test_fp8_bf16_out(gg, bm):
     ref, s = oracle.grouped_gemm_fp8(Aq, a_scale, Bq, b_scale, w.offsets, M_cap=w.M_cap)
     G = _q8_group_max(Aq, a_scale, Bq, b_scale, w.offsets, w.M_cap)
     parity.check_fp8_bf16(c16[:m].float().cpu().numpy(), ref[:m], s[:m], G[:m], w.K, "fp8 bf16-out")
+
+
+@pytest.mark.parametrize("bm", [0, 16, 128])
+def test_fp8_swiglu(gg, bm):
+    # the fp8 x fp8 gate/up product with the SwiGLU epilogue: bracketed by
+    # silu's range over the fp8 bound around the oracle's product, and equal
+    # to the SwiGLU of the fp32 fp8 entry point's output within the fp32
+    # evaluation error
+    w = wl.make_workload(E=4, K=208, N=784, sizes=[300, 0, 45, 517], seed=27, M_cap=870)
+    Aq, a_scale = wl.fp8_activations(w)
+    Bq, b_scale = wl.fp8_weights(w)
+    dev = torch.device("cuda:0")
+    args = [torch.from_numpy(x).to(dev) for x in (Aq, a_scale, Bq, b_scale, w.offsets)]
+    _say("case fp8 swiglu bm=%d" % bm)
+    H = torch.full((w.M_cap, w.N // 2), float("nan"), dtype=torch.bfloat16, device=dev)
+    gg.grouped_gemm_fp8_swiglu(*args, out=H, bm=bm)
+    c32 = gg.grouped_gemm_fp8(*args, bm=bm)
+    torch.cuda.synchronize()
+    m = w.M_tot
+    got = H.float().cpu().numpy().astype(np.float64)
+    assert np.isnan(got[m:]).all()
+    ref, s = oracle.grouped_gemm_fp8(Aq, a_scale, Bq, b_scale, w.offsets, M_cap=w.M_cap)
+    G = _q8_group_max(Aq, a_scale, Bq, b_scale, w.offsets, w.M_cap)
+    err = parity.fp8_bound(s[:m], G[:m], w.K)
+    parity.check_swiglu_bf16(got[:m], ref[:m], s[:m], "fp8 swiglu", err=err)
+    c64 = c32[:m].cpu().numpy().astype(np.float64)
+    h64 = oracle.swiglu_pairs(c64)
+    slack = parity.swiglu_eval_slack(c64, h64)
+    assert (got[:m] >= oracle.round_to_bf16(h64 - slack)).all()
+    assert (got[:m] <= oracle.round_to_bf16(h64 + slack)).all()
 
 
 @pytest.mark.parametrize("name", ["decode", "uniform16k"])

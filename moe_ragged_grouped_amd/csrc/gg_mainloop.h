@@ -25,9 +25,9 @@
 //    LDS (one ds_read_b128 per lane); B is [K][N] N-contiguous, and its
 //    fragments come from ds_read_b64_tr_b16, which transposes a 4 x 16
 //    row-major block per 16-lane group on the way out of LDS. Rows of both
-//    stages are padded by 16 bytes. The transposing read moves about 97 bytes
-//    per clock per CU against 172 for ds_read_b128, so tall wave tiles (fewer
-//    B fragments per flop) are preferred.
+//    stages are padded by 16 bytes. The transposing read moves about 100
+//    bytes per clock per CU, so tall wave tiles (fewer B fragments per flop)
+//    are preferred.
 //  * The accumulator layout of C^T gives every lane 4 consecutive columns of
 //    one row of C, so the epilogue is one 16-byte store (fp32 C) or one 8-byte
 //    store (bf16 C) per lane per block, straight from registers with a
@@ -63,8 +63,13 @@ struct TileCfg {
   static_assert(WTM % 16 == 0 && WTN % 16 == 0 && BK % 32 == 0, "16x16x32 blocks");
   static constexpr int MI = WTM / 16;
   static constexpr int NI = WTN / 16;
-  static constexpr int A_LD = BK + 8;   // LDS row pitch (elements) of the A stage
-  static constexpr int B_LD = BN + 8;   // LDS row pitch (elements) of the B stage
+  // LDS row pitches (elements), rows padded by 16 bytes. B's transposing
+  // reads run at about 100 bytes per clock per CU at 528 or 544 bytes and 32
+  // unpadded (512). A's 16-byte fragment reads run at 110 with the 144-byte
+  // pitch and 210 with 160 bytes, but the wider pitch made the kernel that
+  // holds every height with the combine epilogue spill, for about 1%.
+  static constexpr int A_LD = BK + 8;
+  static constexpr int B_LD = BN + 8;
   static constexpr int A_STAGE = BM * A_LD;
   static constexpr int B_STAGE = BK * B_LD;
   static constexpr int A_CHUNKS = BM * BK / 8;  // 16-byte chunks per K slice
@@ -376,7 +381,11 @@ __device__ __forceinline__ void k_loop(int KT, Ops &ops) {
     // keep the loads ahead of the matrix work (the scheduler would otherwise
     // sink them next to their LDS stores and expose their latency)
     __builtin_amdgcn_sched_barrier(0);
+    // a wave in its matrix phase wins issue arbitration over the SIMD's other
+    // wave, which meanwhile waits on its loads and LDS stores
+    __builtin_amdgcn_s_setprio(1);
     ops.mma(cur);
+    __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (NS == 1) __syncthreads();  // every wave is done reading the stage
     ops.store_a(Slot<(j + 1) % AD>{}, nxt);

@@ -250,9 +250,13 @@ __device__ __forceinline__ void store_b(const u32x4 (&b)[C::B_PER_T], lds_u16 *B
 // Matrix-core work on one LDS stage (BK/32 K steps of 32). The B fragments
 // of a step are read first and kept; the A fragments are streamed one 16-row
 // block at a time, which keeps a tall wave tile's register footprint small.
-template <class C>
+// mid() runs after the first half of the K steps (at the end when there is
+// only one).
+template <class C, class Mid>
 __device__ __forceinline__ void mma_stage(f32x4 (&acc)[C::NI][C::MI], const lds_u16 *As,
-                                          const lds_u16 *Bs, int wm0, int wn0, int lane) {
+                                          const lds_u16 *Bs, int wm0, int wn0, int lane,
+                                          Mid &&mid) {
+  constexpr int KS = C::BK / 32;
   const int g = lane / 16, s = lane % 16;
 #pragma unroll
   for (int ks = 0; ks < C::BK / 32; ++ks) {
@@ -276,7 +280,12 @@ __device__ __forceinline__ void mma_stage(f32x4 (&acc)[C::NI][C::MI], const lds_
     // one K step at a time: hoisting the next step's fragments above this
     // step's products would add their registers on top of the accumulators
     __builtin_amdgcn_sched_barrier(0);
+    if (KS > 1 && ks == KS / 2 - 1) {
+      mid();
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
+  if constexpr (KS == 1) mid();
 }
 
 // The wave's LDS accesses issued so far have completed (so its other lanes
@@ -353,10 +362,21 @@ __device__ __forceinline__ void combine_epilogue(const TileArgs &t, f32x4 (&acc)
 // in-order vmcnt accounting then stores slice s+1 while the loads of later
 // slices stay in flight.
 //
+// Where the loads issue matters. A CU's memory pipeline stays full, so a
+// wave that issues a load can block until a slot frees. A's loads (one slice
+// ahead) go out first, as they need the whole step to land. B's loads (two
+// slices ahead) go out halfway through the matrix work, so that the eight
+// waves do not all block at the step's start. Measured on one box against
+// issuing both at the start: skew16k 178.5 -> 170.6 us, skew2k_wide 320.3 ->
+// 305.5 us, uniform16k 130.8 -> 128.2 us, decode unchanged. Issuing A halfway
+// instead was slower (skew2k_wide 396 us), and splitting both into quarters
+// gained nothing over halves.
+//
 // Ops supplies, for a compile-time staging slot J: load_a(J, kt) and
 // load_b(J, kt) (slice kt, global -> registers), store_a(J, stage) and
-// store_b(J, stage) (registers -> LDS stage), and mma(stage). Ends with a
-// workgroup barrier, so the next tile may refill the stages at once.
+// store_b(J, stage) (registers -> LDS stage), and mma(stage, mid), which runs
+// mid() at its halfway point. Ends with a workgroup barrier, so the next tile
+// may refill the stages at once.
 template <int J>
 using Slot = std::integral_constant<int, J>;
 
@@ -377,14 +397,14 @@ __device__ __forceinline__ void k_loop(int KT, Ops &ops) {
     constexpr int j = decltype(jc)::value;
     constexpr int cur = j % NS, nxt = (j + 1) % NS;
     ops.load_a(Slot<j % AD>{}, kt + AD);
-    ops.load_b(Slot<j % BD>{}, kt + BD);
     // keep the loads ahead of the matrix work (the scheduler would otherwise
     // sink them next to their LDS stores and expose their latency)
     __builtin_amdgcn_sched_barrier(0);
     // a wave in its matrix phase wins issue arbitration over the SIMD's other
     // wave, which meanwhile waits on its loads and LDS stores
     __builtin_amdgcn_s_setprio(1);
-    ops.mma(cur);
+    // B's loads go out halfway through the matrix work rather than with A's
+    ops.mma(cur, [&] { ops.load_b(Slot<j % BD>{}, kt + BD); });
     __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (NS == 1) __syncthreads();  // every wave is done reading the stage
@@ -401,7 +421,7 @@ __device__ __forceinline__ void k_loop(int KT, Ops &ops) {
     if (kt0 + decltype(jc)::value < KT - 1) step(jc, kt0 + decltype(jc)::value);
   });
   // the last slice sits in stage (KT - 1) % NS
-  ops.mma((KT - 1) % NS);
+  ops.mma((KT - 1) % NS, [] {});
   __syncthreads();
 }
 
@@ -426,8 +446,9 @@ struct KOpsBf16 {
   __device__ __forceinline__ void store_b(Slot<J>, int stage) {
     gg::store_b<C>(st.b[J], Bs0 + stage * C::B_STAGE, t.tid);
   }
-  __device__ __forceinline__ void mma(int stage) {
-    mma_stage<C>(*acc, As0 + stage * C::A_STAGE, Bs0 + stage * C::B_STAGE, wm0, wn0, lane);
+  template <class Mid>
+  __device__ __forceinline__ void mma(int stage, Mid &&mid) {
+    mma_stage<C>(*acc, As0 + stage * C::A_STAGE, Bs0 + stage * C::B_STAGE, wm0, wn0, lane, mid);
   }
 };
 

@@ -251,11 +251,12 @@ __device__ __forceinline__ void store_b(const u32x4 (&b)[C::B_PER_T], lds_u16 *B
 // of a step are read first and kept; the A fragments are streamed one 16-row
 // block at a time, which keeps a tall wave tile's register footprint small.
 // mid() runs after the first half of the K steps (at the end when there is
-// only one).
-template <class C, class Mid>
+// only one). blk(mi) runs in the last K step right after the products of
+// 16-row block mi, whose accumulators are then final.
+template <class C, class Mid, class Blk>
 __device__ __forceinline__ void mma_stage(f32x4 (&acc)[C::NI][C::MI], const lds_u16 *As,
                                           const lds_u16 *Bs, int wm0, int wn0, int lane,
-                                          Mid &&mid) {
+                                          Mid &&mid, Blk &&blk) {
   constexpr int KS = C::BK / 32;
   const int g = lane / 16, s = lane % 16;
 #pragma unroll
@@ -276,6 +277,7 @@ __device__ __forceinline__ void mma_stage(f32x4 (&acc)[C::NI][C::MI], const lds_
 #pragma unroll
       for (int ni = 0; ni < C::NI; ++ni)
         acc[ni][mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x[ni], y, acc[ni][mi], 0, 0, 0);
+      if (ks == KS - 1) blk(mi);
     }
     // one K step at a time: hoisting the next step's fragments above this
     // step's products would add their registers on top of the accumulators
@@ -374,14 +376,20 @@ __device__ __forceinline__ void combine_epilogue(const TileArgs &t, f32x4 (&acc)
 //
 // Ops supplies, for a compile-time staging slot J: load_a(J, kt) and
 // load_b(J, kt) (slice kt, global -> registers), store_a(J, stage) and
-// store_b(J, stage) (registers -> LDS stage), and mma(stage, mid), which runs
-// mid() at its halfway point. Ends with a workgroup barrier, so the next tile
-// may refill the stages at once.
+// store_b(J, stage) (registers -> LDS stage), and mma(stage, mid, blk), which
+// runs mid() at its halfway point and, where the operand type supports it,
+// blk(mi) once block mi's accumulators are final. blk is the epilogue of the
+// tile's last slice (a no-op elsewhere). Ends with a workgroup barrier, so the
+// next tile may refill the stages at once.
 template <int J>
 using Slot = std::integral_constant<int, J>;
 
-template <int AD, int BD, int NS, class Ops>
-__device__ __forceinline__ void k_loop(int KT, Ops &ops) {
+struct NoBlk {
+  __device__ __forceinline__ void operator()(int) const {}
+};
+
+template <int AD, int BD, int NS, class Ops, class Blk = NoBlk>
+__device__ __forceinline__ void k_loop(int KT, Ops &ops, Blk &&last_blk = Blk{}) {
   static_for<(AD > BD ? AD : BD)>([&](auto jc) {
     constexpr int j = decltype(jc)::value;
     if constexpr (j < AD) ops.load_a(jc, j);
@@ -404,7 +412,7 @@ __device__ __forceinline__ void k_loop(int KT, Ops &ops) {
     // wave, which meanwhile waits on its loads and LDS stores
     __builtin_amdgcn_s_setprio(1);
     // B's loads go out halfway through the matrix work rather than with A's
-    ops.mma(cur, [&] { ops.load_b(Slot<j % BD>{}, kt + BD); });
+    ops.mma(cur, [&] { ops.load_b(Slot<j % BD>{}, kt + BD); }, NoBlk{});
     __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (NS == 1) __syncthreads();  // every wave is done reading the stage
@@ -421,7 +429,7 @@ __device__ __forceinline__ void k_loop(int KT, Ops &ops) {
     if (kt0 + decltype(jc)::value < KT - 1) step(jc, kt0 + decltype(jc)::value);
   });
   // the last slice sits in stage (KT - 1) % NS
-  ops.mma((KT - 1) % NS, [] {});
+  ops.mma((KT - 1) % NS, [] {}, last_blk);
   __syncthreads();
 }
 
@@ -446,9 +454,10 @@ struct KOpsBf16 {
   __device__ __forceinline__ void store_b(Slot<J>, int stage) {
     gg::store_b<C>(st.b[J], Bs0 + stage * C::B_STAGE, t.tid);
   }
-  template <class Mid>
-  __device__ __forceinline__ void mma(int stage, Mid &&mid) {
-    mma_stage<C>(*acc, As0 + stage * C::A_STAGE, Bs0 + stage * C::B_STAGE, wm0, wn0, lane, mid);
+  template <class Mid, class Blk>
+  __device__ __forceinline__ void mma(int stage, Mid &&mid, Blk &&blk) {
+    mma_stage<C>(*acc, As0 + stage * C::A_STAGE, Bs0 + stage * C::B_STAGE, wm0, wn0, lane, mid,
+                 blk);
   }
 };
 
@@ -478,16 +487,9 @@ __device__ __forceinline__ void run_tile(const TileArgs &t, lds_u16 *lds) {
   init_loads<C, R>(L, t);
   Staging<C> st;
   KOpsBf16<C> ops{L, st, t, As0, Bs0, &acc, wm0, wn0, lane};
-  k_loop<C::AD, C::BD, C::NS>(KT, ops);
-
   // epilogue: lane holds C[m][n..n+3] for m = s, n = 4g within each 16x16 block
   const int g = lane / 16, s = lane % 16;
-  if constexpr (O == Out::AddF32) {
-    combine_epilogue<C>(t, acc, (lds_f32 *)lds, wave, lane, wm0, wn0);
-    return;
-  }
-#pragma unroll
-  for (int mi = 0; mi < C::MI; ++mi) {
+  auto store_block = [&](int mi) {
     const int m = wm0 + mi * 16 + s;
     int dst_row = m;  // row of t.C this lane writes
     if constexpr (R == Rows::Indexed) {
@@ -512,7 +514,24 @@ __device__ __forceinline__ void run_tile(const TileArgs &t, lds_u16 *lds) {
         }
       }
     }
+  };
+  // With bf16 weights and grouped rows, each block is stored during the last
+  // slice's matrix work, as soon as its accumulators are final; the stores
+  // then drain while the later blocks are multiplied. (A gathered row's
+  // destination index or an fp8 column scale would be a global load on that
+  // path, and the combine stages through the LDS the last slice still reads.)
+  constexpr bool kEarly = O != Out::AddF32 && R == Rows::Grouped && !C::FP8B;
+  if constexpr (kEarly) {
+    k_loop<C::AD, C::BD, C::NS>(KT, ops, store_block);
+    return;
   }
+  k_loop<C::AD, C::BD, C::NS>(KT, ops);
+  if constexpr (O == Out::AddF32) {
+    combine_epilogue<C>(t, acc, (lds_f32 *)lds, wave, lane, wm0, wn0);
+    return;
+  }
+#pragma unroll
+  for (int mi = 0; mi < C::MI; ++mi) store_block(mi);
 }
 
 }  // namespace gg

@@ -197,8 +197,9 @@ struct KOpsQ8 {
     store_b_q8<C>(st.b[J], Bs0 + stage * C::B_STAGE, t.tid);
   }
   // one 128-deep K step per stage: mid() (the B loads) runs before it
-  template <class Mid>
-  __device__ __forceinline__ void mma(int stage, Mid &&mid) {
+  // (the fp8 epilogue runs after the loop: blk is not used)
+  template <class Mid, class Blk>
+  __device__ __forceinline__ void mma(int stage, Mid &&mid, Blk &&) {
     mid();
     __builtin_amdgcn_sched_barrier(0);
     mma_stage_q8<C>(*acc, As0 + stage * C::A_STAGE, Bs0 + stage * C::B_STAGE, wm0, wn0, lane);

@@ -146,9 +146,12 @@ __device__ __forceinline__ void store_b_q8(const u32x4 (&b)[C::B_PER_T], lds_u8 
 
 // The 128-deep slice in one stage: B^T operands (32 k of one column per
 // lane) are read first and kept, A^T operands streamed per 16-row block.
-template <class C>
+// blk(mi) runs right after block mi's products (a no-op but in a tile's last
+// slice, where block mi's accumulators are then final).
+template <class C, class Blk>
 __device__ __forceinline__ void mma_stage_q8(f32x4 (&acc)[C::NI][C::MI], const lds_u8 *As,
-                                             const lds_u8 *Bs, int wm0, int wn0, int lane) {
+                                             const lds_u8 *Bs, int wm0, int wn0, int lane,
+                                             Blk &&blk) {
   const int g = lane / 16, s = lane % 16;
   i32x8 x[C::NI];
 #pragma unroll
@@ -172,6 +175,7 @@ __device__ __forceinline__ void mma_stage_q8(f32x4 (&acc)[C::NI][C::MI], const l
       // formats 0, 0 = E4M3 for both operands; block scales 127 = 2^0
       acc[ni][mi] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(x[ni], y, acc[ni][mi], 0, 0,
                                                                      0, 127, 0, 127);
+    blk(mi);
   }
 }
 
@@ -196,13 +200,16 @@ struct KOpsQ8 {
   __device__ __forceinline__ void store_b(Slot<J>, int stage) {
     store_b_q8<C>(st.b[J], Bs0 + stage * C::B_STAGE, t.tid);
   }
-  // one 128-deep K step per stage: mid() (the B loads) runs before it
-  // (the fp8 epilogue runs after the loop: blk is not used)
+  // one 128-deep K step per stage: mid() (the B loads) runs before it, then
+  // blk(-1) (the last slice's epilogue set-up), then the products with
+  // blk(mi) after block mi
   template <class Mid, class Blk>
-  __device__ __forceinline__ void mma(int stage, Mid &&mid, Blk &&) {
+  __device__ __forceinline__ void mma(int stage, Mid &&mid, Blk &&blk) {
     mid();
     __builtin_amdgcn_sched_barrier(0);
-    mma_stage_q8<C>(*acc, As0 + stage * C::A_STAGE, Bs0 + stage * C::B_STAGE, wm0, wn0, lane);
+    blk(-1);
+    mma_stage_q8<C>(*acc, As0 + stage * C::A_STAGE, Bs0 + stage * C::B_STAGE, wm0, wn0, lane,
+                    blk);
   }
 };
 
@@ -232,27 +239,62 @@ __device__ __forceinline__ void run_tile_q8(const TileArgs &t, lds_u16 *lds_base
   init_loads_q8<C>(L, t);
   StagingQ8<C> st;
   KOpsQ8<C> ops{L, st, t, As0, Bs0, &acc, wm0, wn0, lane};
-  k_loop<C::AD, C::BD, 2>(KT, ops);
-
   // epilogue: lane holds C[m][n..n+3] for m = s, n = 4g within each 16x16
-  // block, times the row's activation scale and the columns' weight scales
+  // block, times the row's activation scale and the columns' weight scales.
+  // It runs inside the last slice: blk(-1) loads the scales (the staging
+  // registers are free by then, as no slice follows), and each block is
+  // stored right after its final products, so the stores drain while the
+  // later blocks are multiplied.
   const int g = lane / 16, s = lane % 16;
-#pragma unroll
-  for (int mi = 0; mi < C::MI; ++mi) {
-    const int m = wm0 + mi * 16 + s;
-    if (m < t.rows) {
-      const float sa = ld_g4f(t.a_scale + m);
+  // C (or H) at row m, columns n..n+3, from the scaled accumulators v
+  auto put = [&](int m, int n, f32x4 v) {
+    if constexpr (O == Out::F32)
+      st_g16((float *)t.C + (size_t)m * t.N + n, v);
+    else if constexpr (O == Out::BF16)
+      st_g8_bf16((uint16_t *)t.C + (size_t)m * t.N + n, v);
+    else  // SwiGLU of the (gate, up) pairs (n, n+1), (n+2, n+3), scales applied
+      st_g4_swiglu_bf16((uint16_t *)t.C + (size_t)m * (t.N / 2) + n / 2, v);
+  };
+  f32x4 bsc[C::NI];
+  float asc[C::MI];
+  auto epilogue = [&](int mi) {
+    if (mi < 0) {
 #pragma unroll
       for (int ni = 0; ni < C::NI; ++ni) {
         const int n = wn0 + ni * 16 + 4 * g;
-        if (n < t.ncols) {
-          const f32x4 v = acc[ni][mi] * sa * ld_g16f(t.scale + n);
-          if constexpr (O == Out::F32)
-            st_g16((float *)t.C + (size_t)m * t.N + n, v);
-          else if constexpr (O == Out::BF16)
-            st_g8_bf16((uint16_t *)t.C + (size_t)m * t.N + n, v);
-          else  // SwiGLU of the (gate, up) pairs (n, n+1), (n+2, n+3), scales applied
-            st_g4_swiglu_bf16((uint16_t *)t.C + (size_t)m * (t.N / 2) + n / 2, v);
+        bsc[ni] = n < t.ncols ? ld_g16f(t.scale + n) : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int i = 0; i < C::MI; ++i) {
+        const int m = wm0 + i * 16 + s;
+        asc[i] = m < t.rows ? ld_g4f(t.a_scale + m) : 0.f;
+      }
+      return;
+    }
+    const int m = wm0 + mi * 16 + s;
+    if (m < t.rows) {
+#pragma unroll
+      for (int ni = 0; ni < C::NI; ++ni) {
+        const int n = wn0 + ni * 16 + 4 * g;
+        if (n < t.ncols) put(m, n, acc[ni][mi] * asc[mi] * bsc[ni]);
+      }
+    }
+  };
+  if constexpr (C::MI <= 4) {
+    k_loop<C::AD, C::BD, 2>(KT, ops, epilogue);
+  } else {
+    // the tallest tile's registers do not hold the scales through its last
+    // slice (it spilled): it loads them per block and stores after the loop
+    k_loop<C::AD, C::BD, 2>(KT, ops);
+#pragma unroll
+    for (int mi = 0; mi < C::MI; ++mi) {
+      const int m = wm0 + mi * 16 + s;
+      if (m < t.rows) {
+        const float sa = ld_g4f(t.a_scale + m);
+#pragma unroll
+        for (int ni = 0; ni < C::NI; ++ni) {
+          const int n = wn0 + ni * 16 + 4 * g;
+          if (n < t.ncols) put(m, n, acc[ni][mi] * sa * ld_g16f(t.scale + n));
         }
       }
     }

@@ -994,9 +994,10 @@ def test_fp8_full_size_sampled(gg, name):
 @pytest.mark.parametrize("K", [64, 200])
 def test_many_tiles_per_workgroup(gg, bm, K):
     # 8 experts x ~700 rows x 16 column tiles: hundreds to thousands of tiles,
-    # so every workgroup runs several tiles of one height back to back (the
-    # next tile's first slices are loaded while the current one is stored);
-    # K = 64 is a single slice, K = 200 ends inside the fourth
+    # so every workgroup runs several tiles of one height back to back, each
+    # storing its C blocks during its last K slice; K = 64 is a single slice
+    # (the stores then run inside the first one), K = 200 ends inside the
+    # fourth
     w = wl.make_workload(E=8, K=K, N=4096, sizes=[700, 690, 0, 705, 1, 650, 700, 33], seed=49)
     _full_compare(gg, w, bm, "many-tiles K=%d" % K)
 

@@ -309,7 +309,7 @@ def main():
     weights_key = "fp8a" if args.acts == "fp8" else args.weights
     traffic = measured_traffic(args.config, args.bm, args.out, weights_key, rows_mode)
     # the matrix-core peak of the operand type: fp8 x fp8 on the fp8 cores,
-    # otherwise bf16 (fp8 weights are widened to bf16 before the matrix cores)
+    # otherwise bf16 (fp8 weights are widened to bf16 for the matrix cores)
     mfma_peak = MFMA_FP8_PEAK_TFLOPS if args.acts == "fp8" else MFMA_BF16_PEAK_TFLOPS
     ridge = mfma_peak * 1e12 / (HBM_PEAK_GBS * 1e9)  # flop per byte
     if intensity < ridge:

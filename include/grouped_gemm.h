@@ -212,9 +212,10 @@ gg_status_t gg_grouped_gemm_bf16_gather_combine(const void *X, int32_t n_src,
  *   b_scale  fp32 [E][N] on the device, 16-byte aligned: one scale per expert
  *            and output column.
  *   C        fp32 [M_cap][N].
- * Each fp8 weight is widened exactly to bf16 on its way into LDS, the products
- * accumulate in fp32 in the bf16 matrix cores, and the epilogue multiplies by
- * the column scale (one more fp32 rounding). Weight bytes in HBM are halved;
+ * The weights stay fp8 in LDS and each is widened exactly to bf16 as the
+ * matrix cores' operand is read from there; the products accumulate in fp32
+ * in the bf16 matrix cores, and the epilogue multiplies by the column scale
+ * (one more fp32 rounding). Weight bytes in HBM are halved;
  * this is a separate precision from gg_grouped_gemm_bf16, not a replacement.
  * Other arguments and rules are those of gg_grouped_gemm_bf16; b_scale NULL
  * is GG_ERR_INVALID_VALUE, misaligned b_scale GG_ERR_MISALIGNED.

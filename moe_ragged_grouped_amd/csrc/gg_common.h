@@ -22,6 +22,9 @@ typedef __attribute__((address_space(3))) uint16_t lds_u16;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 typedef __attribute__((address_space(3))) float lds_f32;
 typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+typedef __attribute__((ext_vector_type(2))) int i32x2;
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
 constexpr int kThreads = 512;  // eight 64-lane waves per workgroup
 constexpr int kWave = 64;
@@ -86,20 +89,13 @@ __device__ __forceinline__ float ld_g4f(const float *p) { return *(gbl_cf32 *)p;
 typedef __attribute__((address_space(1))) const f32x4 gbl_cf32x4;
 __device__ __forceinline__ f32x4 ld_g16f(const float *p) { return *(gbl_cf32x4 *)p; }
 
-// 16 fp8 e4m3 values (OCP, as v_cvt_scalef32_pk_bf16_fp8 reads them) ->
-// 16 bf16 values, in order: lo holds elements 0..7, hi 8..15. Each
-// instruction converts the two fp8 bytes of one 16-bit half of a dword; the
-// scale operand is 1, so the conversion is exact.
+// Two fp8 e4m3 values (OCP, as v_cvt_scalef32_pk_bf16_fp8 reads them), the
+// 16-bit half HIGH of a dword, -> two bf16 values in order. The scale
+// operand is 1, so the conversion is exact.
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 template <bool HIGH>
 __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HIGH));
-}
-__device__ __forceinline__ void fp8x16_to_bf16x16(u32x4 in, u32x4 &lo, u32x4 &hi) {
-  lo = u32x4{fp8x2_to_bf16x2<false>(in.x), fp8x2_to_bf16x2<true>(in.x),
-             fp8x2_to_bf16x2<false>(in.y), fp8x2_to_bf16x2<true>(in.y)};
-  hi = u32x4{fp8x2_to_bf16x2<false>(in.z), fp8x2_to_bf16x2<true>(in.z),
-             fp8x2_to_bf16x2<false>(in.w), fp8x2_to_bf16x2<true>(in.w)};
 }
 
 // One 16-byte global store (global_store_dwordx4).

@@ -50,8 +50,9 @@ struct TileCfg {
   static constexpr int NS = NS_;
   static_assert(NS == 1 || NS == 2, "LDS stages");
   static constexpr bool Q8 = false;  // bf16 activations (see gg_mainloop_q8.h)
-  // B in HBM: bf16 (2 bytes) or fp8 e4m3 (1 byte, widened to bf16 on its way
-  // into LDS); one 16-byte global chunk holds B_CE elements of a B row
+  // B in HBM: bf16 (2 bytes) or fp8 e4m3 (1 byte, kept as fp8 in LDS and
+  // widened to bf16 as its operand is read); one 16-byte global chunk holds
+  // B_CE elements of a B row
   static constexpr bool FP8B = FP8B_;
   static constexpr int A_ELEM = 2;  // bytes per A element (bf16)
   static constexpr int B_ELEM = FP8B ? 1 : 2;
@@ -69,9 +70,14 @@ struct TileCfg {
   // pitch and 210 with 160 bytes, but the wider pitch made the kernel that
   // holds every height with the combine epilogue spill, for about 1%.
   static constexpr int A_LD = BK + 8;
-  static constexpr int B_LD = BN + 8;
+  static constexpr int B_LD = BN + 8;  // bf16 B rows, in elements
+  // B row pitch in bytes. fp8 weights stay fp8 in LDS (rows padded by 16
+  // bytes: the 8-bit transposing read runs at about 108 bytes per clock per
+  // CU at 272 bytes, 56 at 264, 16 at 256) and are widened to bf16 after
+  // the read, so that LDS holds and moves half the weight bytes.
+  static constexpr int B_LDB = FP8B ? BN + 16 : 2 * B_LD;
   static constexpr int A_STAGE = BM * A_LD;
-  static constexpr int B_STAGE = BK * B_LD;
+  static constexpr int B_STAGE = BK * B_LDB / 2;  // in 16-bit units
   static constexpr int A_CHUNKS = BM * BK / 8;  // 16-byte chunks per K slice
   static constexpr int B_CHUNKS = BK * BN / B_CE;
   static constexpr int A_PER_T = (A_CHUNKS + kThreads - 1) / kThreads;
@@ -233,15 +239,11 @@ __device__ __forceinline__ void store_b(const u32x4 (&b)[C::B_PER_T], lds_u16 *B
     const int c = tid + i * kThreads;
     const int kr = c / (C::BN / C::B_CE), nc = c % (C::BN / C::B_CE);
     if (C::B_CHUNKS % kThreads == 0 || c < C::B_CHUNKS) {
-      lds_u16 *dst = Bs + kr * C::B_LD + C::B_CE * nc;
       if constexpr (C::FP8B) {
-        // 16 fp8 values -> 16 bf16 (exact: every e4m3 value is a bf16 value)
-        u32x4 lo, hi;
-        fp8x16_to_bf16x16(b[i], lo, hi);
-        *(lds_u32x4 *)dst = lo;
-        *(lds_u32x4 *)(dst + 8) = hi;
+        // 16 fp8 values as they are
+        *(lds_u32x4 *)((lds_u8 *)Bs + kr * C::B_LDB + 16 * nc) = b[i];
       } else {
-        *(lds_u32x4 *)dst = b[i];
+        *(lds_u32x4 *)(Bs + kr * C::B_LD + C::B_CE * nc) = b[i];
       }
     }
   }
@@ -264,11 +266,23 @@ __device__ __forceinline__ void mma_stage(f32x4 (&acc)[C::NI][C::MI], const lds_
     bf16x8 x[C::NI];
 #pragma unroll
     for (int ni = 0; ni < C::NI; ++ni) {
-      const lds_u16 *p = Bs + (ks * 32 + 8 * g + s / 4) * C::B_LD + wn0 + ni * 16 + 4 * (s % 4);
-      const s16x4 lo = lds_read_tr16(p);
-      const s16x4 hi = lds_read_tr16(p + 4 * C::B_LD);
-      const s16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-      x[ni] = __builtin_bit_cast(bf16x8, v);
+      if constexpr (C::FP8B) {
+        // ds_read_b64_tr_b8: lane 16g + s addresses row 8g + s/2, columns
+        // 8(s%2)..+7 of an 8 x 16 byte block and receives column s of its
+        // 8 rows: the 8 k of its operand, widened exactly to bf16
+        const lds_u8 *p = (const lds_u8 *)Bs + (ks * 32 + 8 * g + s / 2) * C::B_LDB + wn0 +
+                          ni * 16 + 8 * (s % 2);
+        const i32x2 q = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2 *)p);
+        const u32x4 w = {fp8x2_to_bf16x2<false>((uint32_t)q.x), fp8x2_to_bf16x2<true>((uint32_t)q.x),
+                         fp8x2_to_bf16x2<false>((uint32_t)q.y), fp8x2_to_bf16x2<true>((uint32_t)q.y)};
+        x[ni] = __builtin_bit_cast(bf16x8, w);
+      } else {
+        const lds_u16 *p = Bs + (ks * 32 + 8 * g + s / 4) * C::B_LD + wn0 + ni * 16 + 4 * (s % 4);
+        const s16x4 lo = lds_read_tr16(p);
+        const s16x4 hi = lds_read_tr16(p + 4 * C::B_LD);
+        const s16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        x[ni] = __builtin_bit_cast(bf16x8, v);
+      }
     }
 #pragma unroll
     for (int mi = 0; mi < C::MI; ++mi) {

@@ -32,9 +32,6 @@
 namespace gg {
 
 typedef __attribute__((ext_vector_type(8))) int i32x8;
-typedef __attribute__((ext_vector_type(2))) int i32x2;
-typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
-typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
 template <int BM_, int WM_, int WN_, int AD_, int BD_, int BN_ = kTileN>
 struct TileCfgQ8 {

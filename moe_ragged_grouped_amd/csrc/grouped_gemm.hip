@@ -29,8 +29,9 @@ namespace gg {
 
 constexpr int kXcds = 8;
 
-// Operand precisions: bf16 A and B; bf16 A with fp8 weights (widened to
-// bf16 on their way into LDS); fp8 A and B on the fp8 matrix cores.
+// Operand precisions: bf16 A and B; bf16 A with fp8 weights (kept as fp8
+// in LDS, widened to bf16 as the operand is read); fp8 A and B on the fp8
+// matrix cores.
 enum Prec : int { kBf16 = 0, kW8 = 1, kW8A8 = 2 };
 
 template <int P, class Bf16Cfg, class W8Cfg, class Q8Cfg>

@@ -4,8 +4,11 @@
 One step = one launch of the whole path (device tile schedule, per-expert tile
 height, bf16 matrix-core K loop, register-direct epilogue) over one batch of
 synthetic, seeded inputs already resident in HBM. Default workload: the
-decode shape of a Mixture-of-Experts layer's share on one GPU (32 experts x 16
-routed rows, K=6144, N=4096).
+uniform large batch of the Blackwell worklog's headline runs (64 experts x 256
+routed rows, K=1024, N=2688, 90.2 GFLOP useful). The other full-size
+workloads (the decode shape, the skewed 16k batch, the small skewed batch
+with wide weights) are timed after it, outside its timed region, and reported
+under "other_configs".
 
 Prints one JSON line:
   value      useful TFLOP/s = 2*M_tot*K*N / (time per step)
@@ -17,10 +20,11 @@ Prints one JSON line:
              measured HBM bytes per launch from the committed rocprofv3
              counter summary, when that summary matches the current kernel
              sources, else null.
-  cpu_baseline  the CPU oracle timed on a bounded sample of the same workload.
+  cpu_baseline  the CPU oracle timed on a bounded sample of the same workload
+             (best of 3 passes on all its threads, and on one thread).
 
-    python bench.py [--steps K] [--warmup W] [--config decode] [--bm 0]
-                    [--out fp32|bf16|swiglu]
+    python bench.py [--steps K] [--warmup W] [--config uniform16k] [--bm 0]
+                    [--out fp32|bf16|swiglu] [--also decode,skew16k,skew2k_wide]
 
 --out bf16 times the bf16-output entry point (C rounded to bf16 in the
 epilogue); its algorithmic bytes count C at 2 bytes per element. --out swiglu
@@ -100,7 +104,13 @@ def measured_traffic(config, bm, out="fp32", weights="bf16", rows="grouped"):
 
 
 def cpu_baseline(w, budget_s=12.0):
-    """Time the CPU oracle on the first n experts of the workload (bounded sample)."""
+    """Time the CPU oracle on a bounded sample of the workload.
+
+    The sample is the first n experts with rows (whole rows, full K and N),
+    n chosen so that one pass takes about a quarter of the budget on all the
+    oracle's threads; the figure is the best of 3 passes. The same is done on
+    one thread with a sample sized to about a tenth of the budget.
+    """
     import numpy as np
 
     import oracle
@@ -111,35 +121,164 @@ def cpu_baseline(w, budget_s=12.0):
         e1 = nz[n - 1] + 1
         off = w.offsets[: e1 + 1].copy()
         rows = int(off[-1])
-        A = w.A[:rows]
-        B = w.B[:e1]
         t0 = time.perf_counter()
-        oracle.grouped_gemm(A, B, off, M_cap=rows)
-        dt = time.perf_counter() - t0
-        return dt, 2.0 * rows * w.K * w.N, rows, e1
+        oracle.grouped_gemm(w.A[:rows], w.B[:e1], off, M_cap=rows)
+        return time.perf_counter() - t0, 2.0 * rows * w.K * w.N, rows, e1
 
-    dt1, _, _, _ = run(1)
-    n = int(max(1, min(len(nz), budget_s / max(dt1, 1e-6))))
-    dt, flops, rows, e1 = run(n)
-    # a whole workload that takes well under the budget is timed over
-    # repeated passes, so that the figure rests on about budget_s of work
-    passes = 1
-    while n == len(nz) and dt < 0.8 * budget_s:
-        more = int(min(50, max(1, (budget_s - dt) / max(dt / passes, 1e-6))))
-        for _ in range(more):
-            d, _, _, _ = run(n)
-            dt += d
-        passes += more
+    def leg(target_s):
+        run(1)  # first touch of the pages
+        dt1 = run(1)[0]
+        n = int(max(1, min(len(nz), target_s / max(dt1, 1e-6))))
+        best = None
+        for _ in range(3):
+            dt, flops, rows, e1 = run(n)
+            best = dt if best is None else min(best, dt)
+        return flops / best / 1e12, best, rows, e1
+
+    threads = oracle.threads()
+    v, dt, rows, e1 = leg(budget_s / 4)
+    oracle.set_threads(1)
+    try:
+        v1, dt1, rows1, e11 = leg(budget_s / 10)
+    finally:
+        oracle.set_threads(threads)
     return {
-        "value": passes * flops / dt / 1e12,
+        "value": v,
         "unit": "TFLOP/s",
-        "cores": oracle.threads(),
+        "cores": threads,
         "kind": "oracle",
-        "sample": "%s of experts 0..%d of the %s workload (%d routed rows, full K=%d and N=%d), "
-                  "fp64 accumulation plus the sum|ab| bound, %.1f s in all" % (
-                      "%d passes" % passes if passes > 1 else "one pass", e1 - 1, w.name, rows,
-                      w.K, w.N, dt),
+        "sample": "experts 0..%d of the %s workload (%d routed rows, full K=%d and N=%d), fp64 "
+                  "accumulation plus the sum|ab| bound, best of 3 passes of %.2f s on %d threads" % (
+                      e1 - 1, w.name, rows, w.K, w.N, dt, threads),
+        "nproc": os.cpu_count(),
+        "one_thread": {"value": v1, "unit": "TFLOP/s",
+                       "sample": "experts 0..%d (%d rows), best of 3 passes of %.2f s" % (
+                           e11 - 1, rows1, dt1)},
     }
+
+
+def prepare(w, args, dev):
+    """Device inputs for one workload and the launch a step makes.
+
+    Returns a dict with the step function and the byte and flop counts of
+    one launch. The inputs are drawn and quantized on the host (untimed)."""
+    import numpy as np
+    import torch
+
+    import moe_ragged_grouped_amd as gg
+    import workloads as wl
+
+    A = torch.from_numpy(w.A.view(np.int16)).to(dev).view(torch.bfloat16)
+    off = torch.from_numpy(w.offsets).to(dev)
+    c_dtype = torch.float32 if args.out == "fp32" else torch.bfloat16
+    C = torch.empty((w.M_cap, w.N // 2 if args.out == "swiglu" else w.N), dtype=c_dtype,
+                    device=dev)
+    B = Bq = Bs = Aq = As = X = perm = gate = None
+    if args.weights == "fp8":
+        # fp8 E4M3 weights with per-(expert, column) fp32 scales, quantized
+        # from the bf16 weights on the host (input recipe, untimed)
+        q_np, sc_np = wl.fp8_weights(w)
+        Bq = torch.from_numpy(q_np).to(dev)
+        Bs = torch.from_numpy(sc_np).to(dev)
+        del q_np
+    else:
+        B = torch.from_numpy(w.B.view(np.int16)).to(dev).view(torch.bfloat16)
+    if args.acts == "fp8":
+        aq_np, as_np = wl.fp8_activations(w)
+        Aq = torch.from_numpy(aq_np).to(dev)
+        As = torch.from_numpy(as_np).to(dev)
+    if args.gather:
+        # rows reached by index: X holds the routed rows in a seeded random
+        # (token) order, grouped row r reads X[perm[r]] and is written back to
+        # C[perm[r]] (top-1 routing: permute in, GEMM, permute out)
+        perm_np = np.random.default_rng(w.seed + 500).permutation(w.M_cap).astype(np.int32)
+        X = torch.empty_like(A)
+        X[torch.from_numpy(perm_np).long().to(dev)] = A
+        perm = torch.from_numpy(perm_np).to(dev)
+        if args.combine:
+            # gate weights in (0, 1]; C accumulates across steps (the kernel's
+            # work does not depend on its values, and clearing it inside the
+            # timed region would time a fill kernel too)
+            gate = torch.from_numpy(np.random.default_rng(w.seed + 501).uniform(
+                0.05, 1.0, w.M_cap).astype(np.float32)).to(dev)
+            C.zero_()
+
+    def step():
+        if args.acts == "fp8" and args.out == "swiglu":
+            gg.grouped_gemm_fp8_swiglu(Aq, As, Bq, Bs, off, out=C, bm=args.bm)
+        elif args.acts == "fp8":
+            gg.grouped_gemm_fp8(Aq, As, Bq, Bs, off, out=C, bm=args.bm)
+        elif args.weights == "fp8":
+            gg.grouped_gemm_fp8w(A, Bq, Bs, off, out=C, bm=args.bm)
+        elif args.combine:
+            gg.grouped_gemm_gather_combine(X, perm, B, off, perm, gate, out=C, bm=args.bm)
+        elif args.gather:
+            gg.grouped_gemm_gather(X, perm, B, off, dst_rows=perm, out=C, bm=args.bm)
+        elif args.out == "swiglu":
+            gg.grouped_gemm_swiglu(A, B, off, out=C, bm=args.bm)
+        else:
+            gg.grouped_gemm(A, B, off, out=C, bm=args.bm)
+
+    useful = 2.0 * w.M_tot * w.K * w.N
+    c_bytes = {"fp32": 4, "bf16": 2, "swiglu": 1}[args.out]  # per product column
+    active = int((w.sizes > 0).sum())
+    b_bytes = 2 * w.K * w.N * active if args.weights == "bf16" else (w.K + 4) * w.N * active
+    a_bytes = 2 * w.M_tot * w.K if args.acts == "bf16" else (w.K + 4) * w.M_tot
+    alg_bytes = (a_bytes + b_bytes + c_bytes * w.M_tot * w.N
+                 + (8 * w.M_tot if args.gather else 0)
+                 # the combine reads each output element before adding, and a weight per row
+                 + (4 * w.M_tot * w.N + 4 * w.M_tot if args.combine else 0))
+    # the matrix-core peak of the operand type: fp8 x fp8 on the fp8 cores,
+    # otherwise bf16 (fp8 weights are widened to bf16 for the matrix cores)
+    mfma_peak = MFMA_FP8_PEAK_TFLOPS if args.acts == "fp8" else MFMA_BF16_PEAK_TFLOPS
+    return {"step": step, "useful": useful, "alg_bytes": alg_bytes, "mfma_peak": mfma_peak,
+            "off": off}
+
+
+def ramp(step, ms):
+    """Untimed launches for at least ms milliseconds; returns their count."""
+    import torch
+    n = 0
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(20):
+            step()
+        n += 20
+        torch.cuda.synchronize()
+    return n
+
+
+def time_launches(step, steps, stream):
+    """Average launch time over steps back-to-back launches (HIP events on the
+    launch stream) and the host's wall time around them."""
+    import torch
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev_s = ev0.elapsed_time(ev1) / 1e3
+    return ev_s / steps, wall
+
+
+def roofline(useful, alg_bytes, launch_s, mfma_peak):
+    """The bound of a launch and its achieved fraction of it."""
+    intensity = useful / alg_bytes
+    hbm_gbs = alg_bytes / launch_s / 1e9
+    tflops = useful / launch_s / 1e12
+    ridge = mfma_peak * 1e12 / (HBM_PEAK_GBS * 1e9)  # flop per byte
+    if intensity < ridge:
+        roof = {"bound": "hbm", "achieved": round(hbm_gbs, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(hbm_gbs / HBM_PEAK_GBS, 4)}
+    else:
+        roof = {"bound": "mfma", "achieved": round(tflops, 1), "peak": mfma_peak,
+                "unit": "TFLOP/s", "frac": round(tflops / mfma_peak, 4)}
+    return roof, hbm_gbs, tflops
 
 
 def main():
@@ -147,7 +286,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="decode", choices=sorted(DESCRIPTIONS))
+    ap.add_argument("--config", default="uniform16k", choices=sorted(DESCRIPTIONS))
+    ap.add_argument("--also", default="decode,skew16k,skew2k_wide",
+                    help="other workloads timed after the headline one, outside its timed "
+                         "region (comma-separated, or none)")
     ap.add_argument("--bm", type=int, default=0, help="0 = per-expert tile height chosen on the device")
     ap.add_argument("--ramp-ms", type=float, default=300.0,
                     help="untimed launches for at least this long before the warmup steps, so "
@@ -177,6 +319,14 @@ def main():
               "runs the kernel on its own experts' share; the exchanges sit outside it); "
               "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+    if args.combine:
+        args.gather = True
+    if args.weights == "fp8" and ((args.out != "fp32" and args.acts == "bf16") or args.gather):
+        raise SystemExit("--weights fp8 times the fp32-output grouped-row entry point")
+    if args.acts == "fp8" and (args.weights != "fp8" or args.gather):
+        raise SystemExit("--acts fp8 needs --weights fp8 and grouped rows")
+    if args.gather and args.out != "fp32":
+        raise SystemExit("--gather times the fp32-output gather entry point")
 
     import numpy as np
     import torch
@@ -200,64 +350,8 @@ def main():
 
     print("bench: drawing workload %s" % args.config, file=sys.stderr, flush=True)
     w = wl.make_workload(args.config)
-    A = torch.from_numpy(w.A.view(np.int16)).to(dev).view(torch.bfloat16)
-    B = torch.from_numpy(w.B.view(np.int16)).to(dev).view(torch.bfloat16)
-    off = torch.from_numpy(w.offsets).to(dev)
-    c_dtype = torch.float32 if args.out == "fp32" else torch.bfloat16
-    C = torch.empty((w.M_cap, w.N // 2 if args.out == "swiglu" else w.N), dtype=c_dtype,
-                    device=dev)
-    if args.weights == "fp8":
-        # fp8 E4M3 weights with per-(expert, column) fp32 scales, quantized
-        # from the bf16 weights on the host (input recipe, untimed)
-        if (args.out != "fp32" and args.acts == "bf16") or args.gather:
-            raise SystemExit("--weights fp8 times the fp32-output grouped-row entry point")
-        q_np, sc_np = wl.fp8_weights(w)
-        Bq = torch.from_numpy(q_np).to(dev)
-        Bs = torch.from_numpy(sc_np).to(dev)
-        del q_np
-    if args.acts == "fp8":
-        if args.weights != "fp8":
-            raise SystemExit("--acts fp8 needs --weights fp8")
-        if args.gather:
-            raise SystemExit("--acts fp8 times the grouped-row entry points")
-        aq_np, as_np = wl.fp8_activations(w)
-        Aq = torch.from_numpy(aq_np).to(dev)
-        As = torch.from_numpy(as_np).to(dev)
-    if args.combine:
-        args.gather = True
-    if args.gather:
-        # rows reached by index: X holds the routed rows in a seeded random
-        # (token) order, grouped row r reads X[perm[r]] and is written back to
-        # C[perm[r]] (top-1 routing: permute in, GEMM, permute out)
-        if args.out != "fp32":
-            raise SystemExit("--gather times the fp32-output gather entry point")
-        perm_np = np.random.default_rng(w.seed + 500).permutation(w.M_cap).astype(np.int32)
-        X = torch.empty_like(A)
-        X[torch.from_numpy(perm_np).long().to(dev)] = A
-        perm = torch.from_numpy(perm_np).to(dev)
-        if args.combine:
-            # gate weights in (0, 1]; Y accumulates across steps (the kernel's
-            # work does not depend on Y's values, and clearing it inside the
-            # timed region would time a fill kernel too)
-            gate = torch.from_numpy(np.random.default_rng(w.seed + 501).uniform(
-                0.05, 1.0, w.M_cap).astype(np.float32)).to(dev)
-            C.zero_()
-
-    def step():
-        if args.acts == "fp8" and args.out == "swiglu":
-            gg.grouped_gemm_fp8_swiglu(Aq, As, Bq, Bs, off, out=C, bm=args.bm)
-        elif args.acts == "fp8":
-            gg.grouped_gemm_fp8(Aq, As, Bq, Bs, off, out=C, bm=args.bm)
-        elif args.weights == "fp8":
-            gg.grouped_gemm_fp8w(A, Bq, Bs, off, out=C, bm=args.bm)
-        elif args.combine:
-            gg.grouped_gemm_gather_combine(X, perm, B, off, perm, gate, out=C, bm=args.bm)
-        elif args.gather:
-            gg.grouped_gemm_gather(X, perm, B, off, dst_rows=perm, out=C, bm=args.bm)
-        elif args.out == "swiglu":
-            gg.grouped_gemm_swiglu(A, B, off, out=C, bm=args.bm)
-        else:
-            gg.grouped_gemm(A, B, off, out=C, bm=args.bm)
+    run = prepare(w, args, dev)
+    step = run["step"]
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream(dev)
@@ -265,13 +359,7 @@ def main():
     # Clock ramp: after the seconds of host-side input generation the GPU sits
     # at idle clocks, and a few milliseconds of warmup launches do not bring
     # it back up (a 10-launch warmup times the 16k shape about 18% slow).
-    ramp_launches = 0
-    t_ramp = time.perf_counter()
-    while (time.perf_counter() - t_ramp) * 1e3 < args.ramp_ms:
-        for _ in range(20):
-            step()
-        ramp_launches += 20
-        torch.cuda.synchronize()
+    ramp_launches = ramp(step, args.ramp_ms)
     print("bench: clock ramp %d launches, warmup %d launches" % (ramp_launches, args.warmup),
           file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -279,53 +367,21 @@ def main():
     torch.cuda.synchronize()
 
     print("bench: timing %d launches" % args.steps, file=sys.stderr, flush=True)
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ev_s = ev0.elapsed_time(ev1) / 1e3
-    step_s = max(wall, ev_s) / args.steps      # the step as the host sees it
-    launch_s = ev_s / args.steps                # average launch on the stream
+    launch_s, wall = time_launches(step, args.steps, stream)
+    step_s = max(wall / args.steps, launch_s)  # the step as the host sees it
 
-    useful = 2.0 * w.M_tot * w.K * w.N
-    c_bytes = {"fp32": 4, "bf16": 2, "swiglu": 1}[args.out]  # per product column
-    active = int((w.sizes > 0).sum())
-    b_bytes = 2 * w.K * w.N * active if args.weights == "bf16" else (w.K + 4) * w.N * active
-    a_bytes = 2 * w.M_tot * w.K if args.acts == "bf16" else (w.K + 4) * w.M_tot
-    alg_bytes = (a_bytes + b_bytes + c_bytes * w.M_tot * w.N
-                 + (8 * w.M_tot if args.gather else 0)
-                 # the combine reads each Y element before adding, and reads a weight per row
-                 + (4 * w.M_tot * w.N + 4 * w.M_tot if args.combine else 0))
-    intensity = useful / alg_bytes
-    hbm_gbs = alg_bytes / launch_s / 1e9
-    tflops_launch = useful / launch_s / 1e12
+    useful, alg_bytes, mfma_peak = run["useful"], run["alg_bytes"], run["mfma_peak"]
+    roof, hbm_gbs, tflops_launch = roofline(useful, alg_bytes, launch_s, mfma_peak)
     rows_mode = "combine" if args.combine else "gather" if args.gather else "grouped"
     weights_key = "fp8a" if args.acts == "fp8" else args.weights
-    traffic = measured_traffic(args.config, args.bm, args.out, weights_key, rows_mode)
-    # the matrix-core peak of the operand type: fp8 x fp8 on the fp8 cores,
-    # otherwise bf16 (fp8 weights are widened to bf16 for the matrix cores)
-    mfma_peak = MFMA_FP8_PEAK_TFLOPS if args.acts == "fp8" else MFMA_BF16_PEAK_TFLOPS
-    ridge = mfma_peak * 1e12 / (HBM_PEAK_GBS * 1e9)  # flop per byte
-    if intensity < ridge:
-        roof = {"bound": "hbm", "achieved": round(hbm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(hbm_gbs / HBM_PEAK_GBS, 4), "traffic": traffic}
-    else:
-        roof = {"bound": "mfma", "achieved": round(tflops_launch, 1), "peak": mfma_peak,
-                "unit": "TFLOP/s", "frac": round(tflops_launch / mfma_peak, 4),
-                "traffic": traffic}
+    roof["traffic"] = measured_traffic(args.config, args.bm, args.out, weights_key, rows_mode)
     roof["kernel"] = KERNEL_NAME
     roof["algorithmic_bytes_per_launch"] = alg_bytes
     roof["avg_launch_us"] = round(launch_s * 1e6, 2)
 
     # the device's tile list for this launch (untimed): tile count, tile
     # heights and row efficiency eta = routed rows / scheduled rows
-    tiles, n_tiles = gg.tile_schedule(off, w.N, w.M_cap, bm=args.bm)
+    tiles, n_tiles = gg.tile_schedule(run["off"], w.N, w.M_cap, bm=args.bm)
     tl = tiles.cpu().numpy()
     first = tl[tl[:, 3] == 0]  # one entry per M tile (its first column tile)
     heights = {int(h): int((first[:, 4] == h).sum()) for h in sorted(set(first[:, 4].tolist()))}
@@ -380,6 +436,35 @@ def main():
         print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
         cpu = cpu_baseline(w)
 
+    # The other full-size workloads with the same entry point, each timed the
+    # same way after its own clock ramp and warmup.
+    others = {}
+    del run, step
+    also = [] if args.also in ("", "none") else args.also.split(",")
+    for name in [x for x in also if x and x != args.config]:
+        if name not in DESCRIPTIONS:
+            raise SystemExit("unknown workload %s" % name)
+        print("bench: drawing workload %s" % name, file=sys.stderr, flush=True)
+        wo = wl.make_workload(name)
+        ro = prepare(wo, args, dev)
+        ro["step"]()
+        ramp(ro["step"], args.ramp_ms)
+        for _ in range(args.warmup):
+            ro["step"]()
+        torch.cuda.synchronize()
+        print("bench: timing %s, %d launches" % (name, args.steps), file=sys.stderr, flush=True)
+        lo, _ = time_launches(ro["step"], args.steps, stream)
+        r_o, gbs_o, tf_o = roofline(ro["useful"], ro["alg_bytes"], lo, ro["mfma_peak"])
+        others[name] = {"workload": DESCRIPTIONS[name], "avg_launch_us": round(lo * 1e6, 2),
+                        "useful_tflops": round(tf_o, 2), "hbm_gbs": round(gbs_o, 1),
+                        "hbm_frac": round(gbs_o / HBM_PEAK_GBS, 4),
+                        "mfma_frac": round(tf_o / ro["mfma_peak"], 4),
+                        "roofline": {"bound": r_o["bound"], "frac": r_o["frac"]},
+                        "algorithmic_bytes_per_launch": ro["alg_bytes"]}
+        del ro, wo
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+
     line = {
         "metric": METRIC,
         "value": round(useful / step_s / 1e12, 2),
@@ -410,6 +495,7 @@ def main():
         "schedule": schedule,
         "timings": extra,
         "cpu_baseline": cpu,
+        "other_configs": others,
     }
     print(json.dumps(line), flush=True)
 

@@ -26,7 +26,10 @@
  *    [0, M_cap]) are the caller's bug; they never make the kernel read or
  *    write outside A[0:M_cap], B[0:E] and C[0:M_cap]: every offset is clamped
  *    into [0, M_cap] and a group whose clamped end precedes its clamped start
- *    is treated as empty.
+ *    is treated as empty. Decreasing offsets can make clamped groups
+ *    overlap; if the tiles of all groups then outnumber what M_cap rows can
+ *    produce with nondecreasing offsets, ((M_cap / h) + E) * ceil(N / 256)
+ *    for the smallest height h in use, the call computes nothing at all.
  *  - Calls on different streams may run concurrently; the library holds no
  *    mutable state besides a per-device cache of launch limits.
  */
@@ -292,7 +295,8 @@ gg_status_t gg_grouped_gemm_fp8_swiglu(const void *Aq, const float *a_scale, con
  * expert's weights). Tiles are 256 columns wide, except when every expert
  * with rows has 16-row tiles: then they are 512 wide. At most
  * max_tiles descriptors are written; *n_tiles (a device int32) receives the
- * full count even when it exceeds max_tiles.
+ * full count even when it exceeds max_tiles (0 for malformed offsets whose
+ * overlapping groups exceed the bound stated at the top of this file).
  * Arguments E, N, M_cap, bm and the offsets rules are those of
  * gg_grouped_gemm_bf16; tiles may be NULL when max_tiles == 0.
  */

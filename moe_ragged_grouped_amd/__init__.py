@@ -14,22 +14,17 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["grouped_gemm", "grouped_gemm_swiglu", "grouped_gemm_gather", "grouped_gemm_gather_combine", "grouped_gemm_fp8w", "grouped_gemm_fp8", "grouped_gemm_fp8_swiglu", "tile_schedule", "library_path", "load_library", "GroupedGemmError",
-           "BM_CHOICES", "TILE_N", "TILE_N_WIDE", "tile_widths", "MAX_EXPERTS", "SYMBOLS"]
+__all__ = ["grouped_gemm", "grouped_gemm_swiglu", "grouped_gemm_gather",
+           "grouped_gemm_gather_combine", "grouped_gemm_fp8w", "grouped_gemm_fp8",
+           "grouped_gemm_fp8_swiglu", "tile_schedule", "library_path", "load_library",
+           "GroupedGemmError", "BM_CHOICES", "TILE_N", "MAX_EXPERTS", "SYMBOLS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libmoe_ragged_grouped_amd.so")
 
 BM_CHOICES = (16, 32, 64, 128, 256)
-TILE_N = 256                      # tile width
-TILE_N_WIDE = 512                 # 16-row tiles when every expert's tiles are 16 rows high
-
-
-def tile_widths(heights, sizes):
-    """Tile width per expert, as the device's schedule picks it: 256, or 512
-    for every expert when each expert with rows has 16-row tiles."""
-    all16 = all(h == 16 for h, m in zip(heights, sizes) if m > 0)
-    return [TILE_N_WIDE if (all16 and h == 16) else TILE_N for h in heights]
+# narrowest tile width: sizes the host-side upper bound of the tile count
+TILE_N = 256
 MAX_EXPERTS = 1024
 SYMBOLS = ("gg_grouped_gemm_bf16", "gg_grouped_gemm_bf16_bf16out", "gg_grouped_gemm_bf16_swiglu",
            "gg_grouped_gemm_bf16_gather", "gg_grouped_gemm_bf16_gather_combine",

@@ -75,7 +75,7 @@ struct Tile {
 // LDS table: exclusive prefix of tile counts per expert (start[E] = total).
 struct SchedLds {
   int start[kMaxExperts + 1];
-  int wave_sum[kThreads / kWave];
+  long long wave_sum[kThreads / kWave];
   int wide16;  // every expert with rows has 16-row tiles: they are kWideN wide
 };
 
@@ -87,8 +87,15 @@ __device__ __forceinline__ int clamp_off(const int32_t *off_g, int e, int M_cap)
 
 // All threads of the workgroup must call this (it contains barriers).
 // bm_fixed = 0 selects adaptive_bm per expert. Returns the total tile count.
+//
+// tile_cap is the host's upper bound of the tile count, derived from M_cap
+// alone: with nondecreasing offsets the segments are disjoint and the count
+// never exceeds it. Offsets that decrease can make clamped segments overlap,
+// each up to M_cap rows, so their counts can sum far past it. The counts are
+// therefore summed in 64 bits, and a launch whose total exceeds tile_cap
+// schedules no tile at all (every later tile index then fits in 32 bits).
 __device__ inline int build_schedule(SchedLds &s, const int32_t *__restrict__ off_g, int E,
-                                     int M_cap, int N, int bm_fixed) {
+                                     int M_cap, int N, int bm_fixed, int tile_cap) {
   const int tid = threadIdx.x;
   // each thread owns a run of consecutive experts (E <= 1024 -> at most 2)
   constexpr int kRun = kMaxExperts / kThreads;
@@ -110,43 +117,45 @@ __device__ inline int build_schedule(SchedLds &s, const int32_t *__restrict__ of
     }
   }
   const bool wide16 = !__syncthreads_or(tall);
-  int cnt[kRun];
-  int local = 0;
+  long long cnt[kRun];
+  long long local = 0;
 #pragma unroll
   for (int j = 0; j < kRun; ++j) {
-    cnt[j] = rows[j] > 0 ? cdiv(rows[j], height[j]) * cdiv(N, width_of(height[j], wide16)) : 0;
+    cnt[j] = rows[j] > 0
+                 ? (long long)cdiv(rows[j], height[j]) * cdiv(N, width_of(height[j], wide16))
+                 : 0;
     local += cnt[j];
   }
   // inclusive scan of 'local' across the 64 lanes of the wave
   const int lane = tid % kWave, wave = tid / kWave;
-  int incl = local;
+  long long incl = local;
 #pragma unroll
   for (int d = 1; d < kWave; d *= 2) {
-    const int y = __shfl_up(incl, d, kWave);
+    const long long y = __shfl_up(incl, d, kWave);
     if (lane >= d) incl += y;
   }
   if (lane == kWave - 1) s.wave_sum[wave] = incl;
   __syncthreads();
-  int before = 0;
+  long long before = 0, total = 0;
 #pragma unroll
-  for (int w = 0; w < kThreads / kWave; ++w)
+  for (int w = 0; w < kThreads / kWave; ++w) {
     if (w < wave) before += s.wave_sum[w];
-  int run = before + incl - local;  // exclusive prefix of this thread's run
+    total += s.wave_sum[w];
+  }
+  if (total > tile_cap) total = 0;  // overlapping malformed segments: no tiles
+  long long run = before + incl - local;  // exclusive prefix of this thread's run
 #pragma unroll
   for (int j = 0; j < kRun; ++j) {
     const int e = e0 + j;
-    if (e < E) s.start[e] = run;
+    if (e < E) s.start[e] = total ? (int)run : 0;
     run += cnt[j];
   }
-  int total = 0;
-#pragma unroll
-  for (int w = 0; w < kThreads / kWave; ++w) total += s.wave_sum[w];
   if (tid == 0) {
-    s.start[E] = total;
+    s.start[E] = (int)total;
     s.wide16 = wide16;
   }
   __syncthreads();
-  return total;
+  return (int)total;
 }
 
 // Decode tile id t (0 <= t < total) into its descriptor.

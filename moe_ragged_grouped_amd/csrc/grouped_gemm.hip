@@ -55,6 +55,7 @@ struct Params {
   const float *a_scale;     // fp8 activations only: [M_cap] per-row scales
   int n_dst;                // indexed form: rows of C (M_cap, or the combine's n_dst)
   const float *row_w;       // combine only: [M_cap] weight of each grouped row
+  int tile_cap;             // upper bound of the tile count (check_sizes)
 };
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
@@ -145,7 +146,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(Params p) {
   // empty asm keeps the compiler from rematerialising it in vector registers)
   uint32_t lds = (uint32_t)(uintptr_t)(lds_u16 *)lds_dyn;
   asm volatile("" : "+s"(lds));
-  const int total = build_schedule(sched, p.off, p.E, p.M_cap, p.N, p.bm_fixed);
+  const int total = build_schedule(sched, p.off, p.E, p.M_cap, p.N, p.bm_fixed, p.tile_cap);
   const int G = gridDim.x;  // a multiple of kXcds
   const int b = blockIdx.x;
   const int slot = (b % kXcds) * (G / kXcds) + b / kXcds;
@@ -174,10 +175,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(Params p) {
 
 __global__ __launch_bounds__(kThreads) void tile_schedule_kernel(const int32_t *off, int E, int N,
                                                                  int M_cap, int bm_fixed,
-                                                                 int32_t *tiles, int32_t *n_tiles,
-                                                                 int max_tiles) {
+                                                                 int tile_cap, int32_t *tiles,
+                                                                 int32_t *n_tiles, int max_tiles) {
   __shared__ SchedLds sched;
-  const int total = build_schedule(sched, off, E, M_cap, N, bm_fixed);
+  const int total = build_schedule(sched, off, E, M_cap, N, bm_fixed, tile_cap);
   if (threadIdx.x == 0) *n_tiles = total;
   const int lim = total < max_tiles ? total : max_tiles;
   for (int t = threadIdx.x; t < lim; t += kThreads) {
@@ -317,6 +318,7 @@ static gg_status_t grouped_gemm(Params p, void *stream) {
     if (!aligned(p.a_scale, 4) || p.K % 16 != 0 || p.N % 16 != 0) return GG_ERR_MISALIGNED;
   }
   if (p.M_cap == 0 || bound == 0) return GG_OK;
+  p.tile_cap = (int)bound;
   hipStream_t s = static_cast<hipStream_t>(stream);
   switch (p.bm_fixed) {
     case 16: return launch<1, O, R, P>(p, bound, s);
@@ -331,7 +333,7 @@ static gg_status_t grouped_gemm(Params p, void *stream) {
 static Params make_params(const void *A, const void *B, const int32_t *off, void *C, int32_t E,
                           int32_t K, int32_t N, int32_t M_cap, int32_t bm) {
   return Params{static_cast<const uint16_t *>(A), static_cast<const uint16_t *>(B), off, C, E, K,
-                N, M_cap, bm, nullptr, nullptr, 0, nullptr, nullptr, M_cap, nullptr};
+                N, M_cap, bm, nullptr, nullptr, 0, nullptr, nullptr, M_cap, nullptr, 0};
 }
 
 }  // namespace gg
@@ -439,8 +441,8 @@ extern "C" gg_status_t gg_tile_schedule(const int32_t *group_offsets, int32_t E,
     return GG_ERR_INVALID_VALUE;
   if (!aligned(n_tiles, 4) || (tiles && !aligned(tiles, 4))) return GG_ERR_MISALIGNED;
   hipLaunchKernelGGL(tile_schedule_kernel, dim3(1), dim3(kThreads), 0,
-                     static_cast<hipStream_t>(stream), group_offsets, E, N, M_cap, bm, tiles,
-                     n_tiles, max_tiles);
+                     static_cast<hipStream_t>(stream), group_offsets, E, N, M_cap, bm,
+                     (int)bound, tiles, n_tiles, max_tiles);
   return hipGetLastError() == hipSuccess ? GG_OK : GG_ERR_LAUNCH;
 }
 

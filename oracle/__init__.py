@@ -27,14 +27,19 @@ Contents
 * ``useful_flops`` / ``algorithmic_bytes``: the worklog's useful-work count
   (section 1: 2*M_tot*K*N) and the compulsory byte count of section 2.1
   (A once, B once per expert that has rows, C once).
-* ``adaptive_bm``: the per-expert tile-height rule of the HIP path, written
-  from its stated definition (see the function).
+* ``adaptive_bm`` / ``tile_widths``: the per-expert tile-height rule and
+  tile-width rule of the HIP path, each written from its stated definition
+  (see the functions).
 * ``grouped_gemm_indexed``: the same product with A rows gathered from X by a
   row index list and C rows scattered by a second list -- the definition
   written out: A = X[src] (zero rows for indices out of range), the grouped
   product, then C[dst[r]] = C_grouped[r]. The permutation around the GEMM is
   the worklog's "What I am measuring" scope note; the indexed form is the
   plain reading of folding it into the loads and stores.
+* ``e4m3_bf16_table`` / ``grouped_gemm_fp8w_whole``: every E4M3 value is
+  exactly a bfloat16 value, so the fp8-weight product of any size is the
+  binary64 triple loop above on the codes' bfloat16 patterns, each column
+  then times its scale (pinned against ``grouped_gemm_fp8w``).
 * ``decode_e4m3`` / ``grouped_gemm_fp8w`` / ``grouped_gemm_fp8w_entries``:
   the fp8-weight product C[r][n] = scale[e][n] * sum_k a[r][k] * dec(q[e][k][n])
   with the OCP E4M3 decode written from the format's definition, and the sum
@@ -112,6 +117,8 @@ def _load():
         lib.oracle_grouped_gemm_entries.restype = i32
         lib.oracle_threads.argtypes = []
         lib.oracle_threads.restype = i32
+        lib.oracle_set_threads.argtypes = [i32]
+        lib.oracle_set_threads.restype = None
         _lib = lib
     return _lib
 
@@ -119,6 +126,11 @@ def _load():
 def threads() -> int:
     """OpenMP threads the oracle runs on."""
     return int(_load().oracle_threads())
+
+
+def set_threads(n: int) -> None:
+    """Run later oracle calls on n OpenMP threads (n >= 1)."""
+    _load().oracle_set_threads(int(n))
 
 
 def _ptr(a: np.ndarray):
@@ -250,6 +262,34 @@ def algorithmic_bytes(sizes, K: int, N: int, c_bytes: int = 4, in_bytes: int = 2
 # Tile heights the HIP path supports, smallest first.
 BM_CHOICES = (16, 32, 64, 128, 256)
 
+# Tile widths (output columns per tile) of the HIP path.
+TILE_WIDTH = 256
+TILE_WIDTH_WIDE = 512
+
+
+def tile_widths(heights, sizes):
+    """Per-expert tile width, as the HIP path defines it.
+
+    Tiles are TILE_WIDTH columns wide. In a launch where every expert that
+    has rows takes 16-row tiles (the weight-streaming case of many small
+    groups), those 16-row tiles are TILE_WIDTH_WIDE columns wide instead.
+    Experts without rows have no tiles and do not take part in the decision.
+    heights and sizes hold one entry per expert (the tile height chosen for
+    it and its row count m_e).
+    """
+    heights = [int(h) for h in heights]
+    sizes = [int(m) for m in sizes]
+    if len(heights) != len(sizes):
+        raise ValueError("one height and one size per expert")
+    every_16 = True
+    for h, m in zip(heights, sizes):
+        if m > 0 and h != 16:
+            every_16 = False
+    widths = []
+    for h in heights:
+        widths.append(TILE_WIDTH_WIDE if (every_16 and h == 16) else TILE_WIDTH)
+    return widths
+
 
 def adaptive_bm(sizes, choices=BM_CHOICES):
     """Per-expert tile height, as the HIP path defines it.
@@ -316,6 +356,53 @@ def decode_e4m3(codes):
     out = sign * mag
     out[(f == 15) & (m == 7)] = np.nan
     return out
+
+
+def e4m3_bf16_table():
+    """bfloat16 bit pattern of every OCP E4M3 code's value, indexed by code.
+
+    An E4M3 value has at most 4 significant bits and an exponent between
+    2^-9 and 2^8, so it is exactly a bfloat16 value (8 significant bits,
+    fp32's exponent range): its binary32 form has zero low 16 bits, and the
+    high 16 bits are its bfloat16 pattern. The two NaN codes map to the
+    bfloat16 quiet NaN 0x7FC0 (sign kept).
+    """
+    v = decode_e4m3(np.arange(256)).astype(np.float32)
+    u = v.view(np.uint32)
+    finite = np.isfinite(v)
+    assert (u[finite] & 0xFFFF == 0).all(), "an E4M3 value that is not a bfloat16 value"
+    bits = (u >> 16).astype(np.uint16)
+    bits[~finite] = np.where(np.arange(256)[~finite] >> 7, 0xFFC0, 0x7FC0).astype(np.uint16)
+    return bits
+
+
+def grouped_gemm_fp8w_whole(A, Bq, scale, offsets, M_cap=None):
+    """The fp8-weight product at any size, through the binary64 triple loop.
+
+    C[r][n] = scale[e][n] * sum_k a[r][k] * dec(q[e][k][n]): dec(q) is taken
+    as the exact bfloat16 value of each code (e4m3_bf16_table), the sum is the
+    C oracle's grouped_gemm, and each column is then multiplied by its scale
+    in binary64. Returns (C, S) like grouped_gemm_fp8w (S scaled by |scale|).
+    Codes must not be NaN.
+    """
+    Bq = np.asarray(Bq, dtype=np.uint8)
+    nan_codes = (Bq & 0x7F) == 0x7F
+    if nan_codes.any():
+        raise ValueError("NaN weight codes")
+    table = e4m3_bf16_table()
+    off = np.asarray(offsets, dtype=np.int32)
+    E, K, N = Bq.shape
+    Bbits = np.empty((E, K, N), dtype=np.uint16)
+    for e in range(E):
+        np.take(table, Bq[e], out=Bbits[e])
+    C, S, _ = grouped_gemm(A, Bbits, off, M_cap=M_cap)
+    sc = np.asarray(scale, dtype=np.float64)
+    for e in range(E):
+        r0, r1 = int(off[e]), int(off[e + 1])
+        if r1 > r0:
+            C[r0:r1] *= sc[e][None, :]
+            S[r0:r1] *= np.abs(sc[e])[None, :]
+    return C, S
 
 
 def _fp8_expert_weights(Bq, scale, e):

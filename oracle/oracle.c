@@ -56,6 +56,15 @@ int oracle_threads(void) {
 #endif
 }
 
+/* Threads later calls run on (n >= 1); used to time the loop on one core. */
+void oracle_set_threads(int n) {
+#ifdef _OPENMP
+  if (n >= 1) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 /*
  * Full grouped product. Returns 0 on success, -1 on malformed offsets
  * (off[0] != 0, decreasing, or off[E] > M_cap). S may be NULL.

@@ -282,6 +282,37 @@ def test_adaptive_bm_special_cases():
     assert oracle.eta(s, oracle.adaptive_bm(s)) >= oracle.eta(s, 128)
 
 
+def test_tile_widths_hand_worked():
+    # every expert with rows takes 16-row tiles: those tiles are 512 wide
+    assert oracle.tile_widths([16, 16, 16], [3, 16, 0]) == [512, 512, 512]
+    # one expert with rows takes taller tiles: every width stays 256
+    assert oracle.tile_widths([16, 32, 16], [5, 20, 1]) == [256, 256, 256]
+    # an expert without rows does not take part, whatever its height
+    assert oracle.tile_widths([16, 256], [7, 0]) == [512, 256]
+    # no rows at all: nothing is tall, 16-row experts would be wide
+    assert oracle.tile_widths([16, 16], [0, 0]) == [512, 512]
+    # a fixed height above 16 never gives wide tiles
+    assert oracle.tile_widths([64, 64], [1, 1]) == [256, 256]
+    # with the adaptive height rule: 32 experts x 16 rows (the decode shape)
+    # are all 16 high, hence 512 wide; one 17-row expert makes all narrow
+    hs = oracle.adaptive_bm([16] * 32)
+    assert oracle.tile_widths(hs, [16] * 32) == [512] * 32
+    sz = [16] * 31 + [17]
+    assert oracle.tile_widths(oracle.adaptive_bm(sz), sz) == [256] * 32
+    with pytest.raises(ValueError):
+        oracle.tile_widths([16], [1, 2])
+
+
+def test_tile_widths_tile_counts():
+    # the decode shape: 32 experts x ceil(4096/512) = 256 tiles; with the
+    # 256-wide rule it would be 512 (one per CU pair)
+    sizes = [16] * 32
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    hs = oracle.adaptive_bm(sizes)
+    assert len(oracle.tile_list(off, 4096, hs, oracle.tile_widths(hs, sizes))) == 256
+    assert len(oracle.tile_list(off, 4096, hs, oracle.TILE_WIDTH)) == 512
+
+
 def test_round_to_bf16_definition_cases():
     # values of the format map to themselves; ties go to the even significand;
     # anything past a tie goes up; the subnormal spacing is 2^-133; the largest
@@ -425,6 +456,48 @@ def test_fp8w_unit_scale_reduces_to_bf16_product():
     m = w.M_tot
     assert np.allclose(c[:m], c0[:m], rtol=0, atol=1e-12 * s0[:m].max())
     assert np.allclose(s[:m], s0[:m], rtol=1e-14)
+
+
+def test_e4m3_bf16_table_against_torch():
+    # the bfloat16 pattern of every finite code is torch's own conversion of
+    # the same value, and widening it back gives the code's value exactly
+    torch = pytest.importorskip("torch")
+    t = oracle.e4m3_bf16_table()
+    vals = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).float()
+    ref = vals.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    finite = np.isfinite(vals.numpy())
+    assert (t[finite] == ref[finite]).all()
+    back = wl.bf16_bits_to_f32(t).astype(np.float64)
+    assert (back[finite] == oracle.decode_e4m3(np.arange(256))[finite]).all()
+    assert t[0x38] == 0x3F80 and t[0xB8] == 0xBF80 and t[0x7E] == 0x43E0  # 1, -1, 448
+
+
+def test_fp8w_whole_matches_definition():
+    # the whole-size route (codes as bf16 patterns, C triple loop, column
+    # scales) against the definition written with numpy products
+    w = wl.make_workload(E=4, K=72, N=48, sizes=[6, 0, 13, 2], seed=40, M_cap=24)
+    q, scale = wl.fp8_weights(w)
+    c0, s0 = oracle.grouped_gemm_fp8w(w.A, q, scale, w.offsets)
+    c1, s1 = oracle.grouped_gemm_fp8w_whole(w.A, q, scale, w.offsets)
+    m = w.M_tot
+    tol = 72 * 2.0 ** -52 * s0[:m]
+    assert (np.abs(c1[:m] - c0[:m]) <= tol).all()
+    assert np.allclose(s1[:m], s0[:m], rtol=1e-14, atol=0)
+    assert np.isnan(c1[m:]).all()
+    # integer codes with power-of-two scales: exact, both ways
+    rng = np.random.default_rng(41)
+    qv = rng.integers(-3, 4, size=(2, 9, 7))
+    Bq = _int_codes(qv)
+    sc = np.ldexp(1.0, rng.integers(-2, 3, size=(2, 7))).astype(np.float32)
+    A = wl.f32_to_bf16_bits(rng.integers(-3, 4, size=(5, 9)).astype(np.float32))
+    off = wl.offsets_from_sizes([3, 2])
+    a, _ = oracle.grouped_gemm_fp8w(A, Bq, sc, off)
+    b, _ = oracle.grouped_gemm_fp8w_whole(A, Bq, sc, off)
+    assert np.array_equal(a, b)
+    with pytest.raises(ValueError):
+        bad = Bq.copy()
+        bad[0, 0, 0] = 0x7F
+        oracle.grouped_gemm_fp8w_whole(A, bad, sc, off)
 
 
 def test_fp8w_column_scale_is_linear_and_entries_match():

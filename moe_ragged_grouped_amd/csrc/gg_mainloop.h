@@ -25,9 +25,10 @@
 //    LDS (one ds_read_b128 per lane); B is [K][N] N-contiguous, and its
 //    fragments come from ds_read_b64_tr_b16, which transposes a 4 x 16
 //    row-major block per 16-lane group on the way out of LDS. Rows of both
-//    stages are padded by 16 bytes. The transposing read moves about 100
-//    bytes per clock per CU, so tall wave tiles (fewer B fragments per flop)
-//    are preferred.
+//    operands are XOR-swizzled by 16-byte chunks (a_chunk, b_chunk below), so
+//    no fragment read has a bank conflict. The transposing read moves at most
+//    about 128 bytes per clock per CU (half the 16-byte read's rate), so
+//    tall wave tiles (fewer B fragments per flop) are preferred.
 //  * The accumulator layout of C^T gives every lane 4 consecutive columns of
 //    one row of C, so the epilogue is one 16-byte store (fp32 C) or one 8-byte
 //    store (bf16 C) per lane per block, straight from registers with a
@@ -64,17 +65,30 @@ struct TileCfg {
   static_assert(WTM % 16 == 0 && WTN % 16 == 0 && BK % 32 == 0, "16x16x32 blocks");
   static constexpr int MI = WTM / 16;
   static constexpr int NI = WTN / 16;
-  // LDS row pitches (elements), rows padded by 16 bytes. B's transposing
-  // reads run at about 100 bytes per clock per CU at 528 or 544 bytes and 32
-  // unpadded (512). A's 16-byte fragment reads run at 110 with the 144-byte
-  // pitch and 210 with 160 bytes, but the wider pitch made the kernel that
-  // holds every height with the combine epilogue spill, for about 1%.
-  static constexpr int A_LD = BK + 8;
-  static constexpr int B_LD = BN + 8;  // bf16 B rows, in elements
-  // B row pitch in bytes. fp8 weights stay fp8 in LDS (rows padded by 16
-  // bytes: the 8-bit transposing read runs at about 108 bytes per clock per
-  // CU at 272 bytes, 56 at 264, 16 at 256) and are widened to bf16 after
-  // the read, so that LDS holds and moves half the weight bytes.
+  // LDS row pitches (elements). Both operands' rows are XOR-swizzled by
+  // 16-byte chunks so that a fragment read touches every bank once:
+  //  * A rows are unpadded (BK elements, A_CH chunks); chunk c of row r sits
+  //    at chunk c ^ (r % A_CH) (a_chunk). Measured with the kernel's own lane
+  //    addresses (eight waves per CU): 4 LDS cycles per ds_read_b128, none
+  //    of them bank conflicts, 234 bytes per clock per CU; rows padded to 144
+  //    bytes (or 272 for 128-deep slices) take 8 cycles, half of them
+  //    conflicts, 128 bytes per clock.
+  //  * bf16 B rows are unpadded (BN elements); chunk c of row k sits at
+  //    chunk c ^ b_swz(k) (b_chunk): 2 LDS cycles per ds_read_b64_tr_b16, no
+  //    conflicts, against 4 cycles, half of them conflicts, with rows padded
+  //    by 16 bytes (the 8-byte reads move at most 111-128 bytes per clock per
+  //    CU either way).
+  // Stores (ds_write_b128) take 8 cycles per instruction, counted as
+  // conflict-free, with every layout here.
+  static constexpr int A_LD = BK;
+  static constexpr int A_CH = BK / 8;
+  static_assert(A_CH == 8 || A_CH == 16, "A swizzle: 8 or 16 chunks per row");
+  static constexpr int B_LD = BN;  // bf16 B rows, in elements
+  // B row pitch in bytes. fp8 weights stay fp8 in LDS and are widened to
+  // bf16 after the read, so that LDS holds and moves half the weight bytes.
+  // Rows are padded by 16 bytes: the 8-bit transposing read then takes 2 LDS
+  // cycles with no conflicts (32 bytes of padding: 4 cycles, half of them
+  // conflicts; none: 32 cycles).
   static constexpr int B_LDB = FP8B ? BN + 16 : 2 * B_LD;
   static constexpr int A_STAGE = BM * A_LD;
   static constexpr int B_STAGE = BK * B_LDB / 2;  // in 16-bit units
@@ -220,17 +234,31 @@ __device__ __forceinline__ void load_b(u32x4 (&b)[C::B_PER_T], const Loads<C> &L
   for (int i = 0; i < C::B_PER_T; ++i) b[i] = ld_buf16<kCacheStream>(r, L.b_off[i], 0u);
 }
 
+// LDS chunk that holds 16-byte chunk c of A row r (the swizzle of TileCfg).
+template <class C>
+__device__ __forceinline__ int a_chunk(int r, int c) {
+  return c ^ (r & (C::A_CH - 1));
+}
+
 // Registers -> one LDS stage.
 template <class C>
 __device__ __forceinline__ void store_a(const u32x4 (&a)[C::A_PER_T], lds_u16 *As, int tid) {
 #pragma unroll
   for (int i = 0; i < C::A_PER_T; ++i) {
     const int c = tid + i * kThreads;
-    const int r = c / (C::BK / 8), kc = c % (C::BK / 8);
+    const int r = c / C::A_CH, kc = c % C::A_CH;
     if (C::A_CHUNKS % kThreads == 0 || c < C::A_CHUNKS)
-      *(lds_u32x4 *)(As + r * C::A_LD + 8 * kc) = a[i];
+      *(lds_u32x4 *)(As + r * C::A_LD + 8 * a_chunk<C>(r, kc)) = a[i];
   }
 }
+
+// LDS chunk that holds 16-byte chunk c (columns 8c .. 8c + 7) of bf16 B row
+// k. A transposing read instruction touches 16 rows, 8g + k' for lane group
+// g (and 8g + 4 + k' for its second half), k' < 4, 32 bytes of each; the
+// XOR moves those 32-byte pieces of rows k' and 8 + k' to eight different
+// places within 256 bytes.
+__device__ __forceinline__ int b_swz(int k) { return ((k & 3) << 1) | (((k >> 3) & 1) << 3); }
+__device__ __forceinline__ int b_chunk(int k, int c) { return c ^ b_swz(k); }
 
 template <class C>
 __device__ __forceinline__ void store_b(const u32x4 (&b)[C::B_PER_T], lds_u16 *Bs, int tid) {
@@ -243,7 +271,7 @@ __device__ __forceinline__ void store_b(const u32x4 (&b)[C::B_PER_T], lds_u16 *B
         // 16 fp8 values as they are
         *(lds_u32x4 *)((lds_u8 *)Bs + kr * C::B_LDB + 16 * nc) = b[i];
       } else {
-        *(lds_u32x4 *)(Bs + kr * C::B_LD + C::B_CE * nc) = b[i];
+        *(lds_u32x4 *)(Bs + kr * C::B_LD + 8 * b_chunk(kr, nc)) = b[i];
       }
     }
   }
@@ -261,6 +289,17 @@ __device__ __forceinline__ void mma_stage(f32x4 (&acc)[C::NI][C::MI], const lds_
                                           Mid &&mid, Blk &&blk) {
   constexpr int KS = C::BK / 32;
   const int g = lane / 16, s = lane % 16;
+  // bf16 B: byte address of this lane's first transposing read of column
+  // block 0 (row 8g + s/4, columns wn0 + 4 (s % 4) ..). The swizzle puts
+  // block ni's 32 bytes at block (ni ^ (s/4)) of the row's 32-byte pieces,
+  // and nothing else sets address bits 5-6 (stage bases and rows are
+  // 512-byte aligned), so block ni's address is this one XOR 32 ni.
+  uint32_t b_base = 0;
+  if constexpr (!C::FP8B) {
+    static_assert(C::B_LD * 2 % 512 == 0 && C::B_STAGE * 2 % 512 == 0, "B rows, stages");
+    const int k = 8 * g + s / 4, n = wn0 + 4 * (s % 4);
+    b_base = (uint32_t)(uintptr_t)(Bs + k * C::B_LD + 8 * b_chunk(k, n / 8) + n % 8);
+  }
 #pragma unroll
   for (int ks = 0; ks < C::BK / 32; ++ks) {
     bf16x8 x[C::NI];
@@ -277,7 +316,9 @@ __device__ __forceinline__ void mma_stage(f32x4 (&acc)[C::NI][C::MI], const lds_
                          fp8x2_to_bf16x2<false>((uint32_t)q.y), fp8x2_to_bf16x2<true>((uint32_t)q.y)};
         x[ni] = __builtin_bit_cast(bf16x8, w);
       } else {
-        const lds_u16 *p = Bs + (ks * 32 + 8 * g + s / 4) * C::B_LD + wn0 + ni * 16 + 4 * (s % 4);
+        // rows 32 ks + 8g + s/4 and + 4 (the swizzle of a row depends only
+        // on its bits 0, 1 and 3), column block ni
+        const lds_u16 *p = (const lds_u16 *)(uintptr_t)(b_base ^ (32u * ni)) + ks * 32 * C::B_LD;
         const s16x4 lo = lds_read_tr16(p);
         const s16x4 hi = lds_read_tr16(p + 4 * C::B_LD);
         const s16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -286,7 +327,8 @@ __device__ __forceinline__ void mma_stage(f32x4 (&acc)[C::NI][C::MI], const lds_
     }
 #pragma unroll
     for (int mi = 0; mi < C::MI; ++mi) {
-      const lds_u16 *p = As + (wm0 + mi * 16 + s) * C::A_LD + ks * 32 + 8 * g;
+      // row wm0 + mi * 16 + s (wm0 is a multiple of 16), chunk 4 ks + g
+      const lds_u16 *p = As + (wm0 + mi * 16 + s) * C::A_LD + 8 * a_chunk<C>(s, 4 * ks + g);
       const bf16x8 y = __builtin_bit_cast(bf16x8, *(const lds_u32x4 *)p);
 #pragma unroll
       for (int ni = 0; ni < C::NI; ++ni)

@@ -76,6 +76,7 @@ struct Tile {
 struct SchedLds {
   int start[kMaxExperts + 1];
   long long wave_sum[kThreads / kWave];
+  int wave_tall[kThreads / kWave];  // a wave saw an expert with rows and taller tiles
   int wide16;  // every expert with rows has 16-row tiles: they are kWideN wide
 };
 
@@ -116,7 +117,16 @@ __device__ inline int build_schedule(SchedLds &s, const int32_t *__restrict__ of
       lo = hi;
     }
   }
-  const bool wide16 = !__syncthreads_or(tall);
+  // workgroup-wide OR of 'tall' through one LDS word per wave (a library
+  // reduction would reserve LDS of its own ahead of the operand stages)
+  const int lane = tid % kWave, wave = tid / kWave;
+  const bool wave_tall = __any(tall);
+  if (lane == 0) s.wave_tall[wave] = wave_tall;
+  __syncthreads();
+  bool any_tall = false;
+#pragma unroll
+  for (int w = 0; w < kThreads / kWave; ++w) any_tall |= s.wave_tall[w] != 0;
+  const bool wide16 = !any_tall;
   long long cnt[kRun];
   long long local = 0;
 #pragma unroll
@@ -127,7 +137,6 @@ __device__ inline int build_schedule(SchedLds &s, const int32_t *__restrict__ of
     local += cnt[j];
   }
   // inclusive scan of 'local' across the 64 lanes of the wave
-  const int lane = tid % kWave, wave = tid / kWave;
   long long incl = local;
 #pragma unroll
   for (int d = 1; d < kWave; d *= 2) {

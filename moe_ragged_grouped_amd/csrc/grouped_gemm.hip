@@ -133,15 +133,38 @@ __device__ __forceinline__ void tile_call(const Params &p, const Tile &t, uint32
   tile_body<Cfg, O, R>(p, t.row0, t.rows, t.col0, t.expert, lds_addr);
 }
 
+// LDS stage bytes a launch needs: the largest of the heights it compiles in.
+template <int MASK, int P>
+constexpr int lds_bytes() {
+  int m = 0;
+  if (MASK & 1) m = m > Pick<P, Cfg16, Cfg16F, CfgQ16>::LDS_BYTES ? m : Pick<P, Cfg16, Cfg16F, CfgQ16>::LDS_BYTES;
+  if (MASK & 1) m = m > Pick<P, Cfg16W, Cfg16FW, CfgQ16W>::LDS_BYTES ? m : Pick<P, Cfg16W, Cfg16FW, CfgQ16W>::LDS_BYTES;
+  if (MASK & 2) m = m > Pick<P, Cfg32, Cfg32F, CfgQ32>::LDS_BYTES ? m : Pick<P, Cfg32, Cfg32F, CfgQ32>::LDS_BYTES;
+  if (MASK & 4) m = m > Pick<P, Cfg64, Cfg64F, CfgQ64>::LDS_BYTES ? m : Pick<P, Cfg64, Cfg64F, CfgQ64>::LDS_BYTES;
+  if (MASK & 8)
+    m = m > Pick<P, Cfg128, Cfg128F, CfgQ128>::LDS_BYTES ? m : Pick<P, Cfg128, Cfg128F, CfgQ128>::LDS_BYTES;
+  if (MASK & 16)
+    m = m > Pick<P, Cfg256, Cfg256F, CfgQ256>::LDS_BYTES ? m : Pick<P, Cfg256, Cfg256F, CfgQ256>::LDS_BYTES;
+  return m;
+}
+
 // MASK bit c compiles in tile height 16 << c (16, 32, 64, 128, 256). A launch
 // must compile in every height its schedule can produce. O is the element
 // type of C; R says whether rows are grouped or gathered/scattered by index;
 // P selects the operand precisions (bf16; fp8 weights; fp8 weights and
 // activations).
+// The launch's LDS: the operand stages from address 0 (the swizzled layouts
+// assume 512-byte aligned stages), then the schedule table.
+template <int MASK, int P>
+constexpr int sched_offset() { return (lds_bytes<MASK, P>() + 15) / 16 * 16; }
+template <int MASK, int P>
+constexpr int launch_lds_bytes() { return sched_offset<MASK, P>() + (int)sizeof(SchedLds); }
+
 template <int MASK, Out O, Rows R, int P>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(Params p) {
+  // the kernel declares no static LDS, so this region starts at address 0
   extern __shared__ __attribute__((aligned(16))) uint16_t lds_dyn[];
-  __shared__ SchedLds sched;
+  SchedLds &sched = *(SchedLds *)((char *)lds_dyn + sched_offset<MASK, P>());
   // the LDS base as a plain byte address pinned in a scalar register (the
   // empty asm keeps the compiler from rematerialising it in vector registers)
   uint32_t lds = (uint32_t)(uintptr_t)(lds_u16 *)lds_dyn;
@@ -192,27 +215,11 @@ __global__ __launch_bounds__(kThreads) void tile_schedule_kernel(const int32_t *
   }
 }
 
-// Dynamic LDS a launch needs: the largest of the heights it compiles in.
-template <int MASK, int P>
-constexpr int lds_bytes() {
-  int m = 0;
-  if (MASK & 1) m = m > Pick<P, Cfg16, Cfg16F, CfgQ16>::LDS_BYTES ? m : Pick<P, Cfg16, Cfg16F, CfgQ16>::LDS_BYTES;
-  if (MASK & 1) m = m > Pick<P, Cfg16W, Cfg16FW, CfgQ16W>::LDS_BYTES ? m : Pick<P, Cfg16W, Cfg16FW, CfgQ16W>::LDS_BYTES;
-  if (MASK & 2) m = m > Pick<P, Cfg32, Cfg32F, CfgQ32>::LDS_BYTES ? m : Pick<P, Cfg32, Cfg32F, CfgQ32>::LDS_BYTES;
-  if (MASK & 4) m = m > Pick<P, Cfg64, Cfg64F, CfgQ64>::LDS_BYTES ? m : Pick<P, Cfg64, Cfg64F, CfgQ64>::LDS_BYTES;
-  if (MASK & 8)
-    m = m > Pick<P, Cfg128, Cfg128F, CfgQ128>::LDS_BYTES ? m : Pick<P, Cfg128, Cfg128F, CfgQ128>::LDS_BYTES;
-  if (MASK & 16)
-    m = m > Pick<P, Cfg256, Cfg256F, CfgQ256>::LDS_BYTES ? m : Pick<P, Cfg256, Cfg256F, CfgQ256>::LDS_BYTES;
-  return m;
-}
-
-// Every launch's LDS (dynamic stages + the static schedule table) must fit
-// one CU's 160 KiB.
+// Every launch's LDS (stages + the schedule table) must fit one CU's 160 KiB.
 constexpr int kLdsPerCu = 160 * 1024;
-static_assert(lds_bytes<31, kBf16>() + (int)sizeof(SchedLds) <= kLdsPerCu, "LDS budget");
-static_assert(lds_bytes<31, kW8>() + (int)sizeof(SchedLds) <= kLdsPerCu, "LDS budget");
-static_assert(lds_bytes<31, kW8A8>() + (int)sizeof(SchedLds) <= kLdsPerCu, "LDS budget");
+static_assert(launch_lds_bytes<31, kBf16>() <= kLdsPerCu, "LDS budget");
+static_assert(launch_lds_bytes<31, kW8>() <= kLdsPerCu, "LDS budget");
+static_assert(launch_lds_bytes<31, kW8A8>() <= kLdsPerCu, "LDS budget");
 
 // Per-device, per-variant launch limits (CU count x resident workgroups).
 struct LaunchInfo {
@@ -229,7 +236,7 @@ static LaunchInfo launch_info(int dev) {
   std::call_once(once[dev], [dev]() {
     LaunchInfo li;
     int cus = 0, per_cu = 0;
-    const int lds = lds_bytes<MASK, P>();
+    const int lds = launch_lds_bytes<MASK, P>();
     li.err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (li.err == hipSuccess)
       li.err = hipFuncSetAttribute((const void *)grouped_gemm_kernel<MASK, O, R, P>,
@@ -256,7 +263,7 @@ static gg_status_t launch(const Params &p, long long tile_bound, hipStream_t str
   if (li.err != hipSuccess) return GG_ERR_LAUNCH;
   long long g = tile_bound < li.grid ? tile_bound : li.grid;
   g = (g + kXcds - 1) / kXcds * kXcds;  // keep a multiple of the XCD count
-  constexpr int lds = lds_bytes<MASK, P>();
+  constexpr int lds = launch_lds_bytes<MASK, P>();
   hipLaunchKernelGGL((grouped_gemm_kernel<MASK, O, R, P>), dim3((unsigned)g), dim3(kThreads),
                      lds, stream, p);
   return hipGetLastError() == hipSuccess ? GG_OK : GG_ERR_LAUNCH;

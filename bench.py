@@ -232,7 +232,71 @@ def prepare(w, args, dev):
     # otherwise bf16 (fp8 weights are widened to bf16 for the matrix cores)
     mfma_peak = MFMA_FP8_PEAK_TFLOPS if args.acts == "fp8" else MFMA_BF16_PEAK_TFLOPS
     return {"step": step, "useful": useful, "alg_bytes": alg_bytes, "mfma_peak": mfma_peak,
-            "off": off}
+            "off": off, "A": A, "B": B, "C": C}
+
+
+def library_yardstick(w, run, args, stream):
+    """The same products through the vendor GEMM library (hipBLASLt via torch),
+    timed like the grouped launch, on the same resident bf16 inputs and with
+    fp32 outputs: a strided-batched product when every expert has the same row
+    count, and one library GEMM per expert with rows (the E launches a grouped
+    GEMM replaces). A measuring stick only: nothing of it is the library's
+    path, and its results are not compared."""
+    import numpy as np
+    import torch
+
+    A, B = run["A"], run["B"]
+    C = torch.empty((w.M_cap, w.N), dtype=torch.float32, device=A.device)
+    off = [int(x) for x in w.offsets]
+    experts = [e for e in range(w.E) if off[e + 1] > off[e]]
+    cases = {}
+    if len(set(int(off[e + 1] - off[e]) for e in range(w.E))) == 1 and w.M_tot > 0:
+        m = w.M_tot // w.E
+        A3 = A[: w.M_tot].view(w.E, m, w.K)
+        C3 = C[: w.M_tot].view(w.E, m, w.N)
+        cases["bmm_strided_batched"] = lambda: torch.bmm(A3, B, out_dtype=torch.float32, out=C3)
+    views = [(A[off[e]:off[e + 1]], B[e], C[off[e]:off[e + 1]]) for e in experts]
+
+    def loop():
+        for a, b, c in views:
+            torch.mm(a, b, out_dtype=torch.float32, out=c)
+    cases["mm_per_expert_loop"] = loop
+    # the same loop captured in a HIP graph: the host's per-launch cost drops out
+    loop()
+    gs = torch.cuda.Stream(A.device)
+    gs.wait_stream(stream)
+    with torch.cuda.stream(gs):
+        loop()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=gs):
+        loop()
+    torch.cuda.synchronize()
+    cases["mm_per_expert_loop_graph"] = graph.replay
+    cases["grouped_gemm (this library)"] = run["step"]
+    out = {}
+    for name, f in cases.items():
+        f()
+        ramp(f, args.ramp_ms)
+        for _ in range(args.warmup):
+            f()
+        t, _ = time_launches(f, args.steps, stream)
+        out[name] = {"avg_us": round(t * 1e6, 2),
+                     "useful_tflops": round(2.0 * w.M_tot * w.K * w.N / t / 1e12, 2),
+                     "launches": len(views) if name.startswith("mm_per_expert") else 1}
+    del graph
+    # the library's rate on a large square bf16 product (bf16 output), for
+    # scale: what its kernels reach where the shape does not limit them
+    n = 8192
+    X = torch.randn(n, n, device=A.device).to(torch.bfloat16)
+    Y = torch.randn(n, n, device=A.device).to(torch.bfloat16)
+    Z = torch.empty(n, n, device=A.device, dtype=torch.bfloat16)
+    sq = lambda: torch.mm(X, Y, out=Z)
+    ramp(sq, args.ramp_ms)
+    t, _ = time_launches(sq, 10, stream)
+    out["square_8192_bf16_mm"] = {"avg_us": round(t * 1e6, 2),
+                                  "tflops": round(2.0 * n ** 3 / t / 1e12, 2), "launches": 1}
+    return out
 
 
 def ramp(step, ms):
@@ -312,6 +376,9 @@ def main():
                     help="skip the graph-captured and cold-cache timings")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (for counter calibration)")
+    ap.add_argument("--library-yardstick", action="store_true",
+                    help="time only the same products through hipBLASLt (torch) beside this "
+                         "library's launch (bf16 weights, fp32 output, grouped rows)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -355,6 +422,13 @@ def main():
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream(dev)
+    if args.library_yardstick:
+        if args.weights != "bf16" or args.out != "fp32" or args.gather:
+            raise SystemExit("--library-yardstick times bf16 weights, fp32 C, grouped rows")
+        print(json.dumps({"library_yardstick": library_yardstick(w, run, args, stream),
+                          "workload": DESCRIPTIONS[args.config], "name": args.config,
+                          "steps": args.steps, "warmup": args.warmup}), flush=True)
+        return
     step()  # correctness launch position of the protocol
     # Clock ramp: after the seconds of host-side input generation the GPU sits
     # at idle clocks, and a few milliseconds of warmup launches do not bring

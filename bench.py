@@ -376,6 +376,9 @@ def main():
                     help="skip the graph-captured and cold-cache timings")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (for counter calibration)")
+    ap.add_argument("--hbm-ceiling", action="store_true",
+                    help="time only plain device-wide streams (a 1 GiB copy and a 1 GiB "
+                         "read-only reduction through torch) for the box's practical HBM rate")
     ap.add_argument("--library-yardstick", action="store_true",
                     help="time only the same products through hipBLASLt (torch) beside this "
                          "library's launch (bf16 weights, fp32 output, grouped rows)")
@@ -413,6 +416,23 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n,
                           "launches": 5}))
+        return
+
+    if args.hbm_ceiling:
+        n = 1 << 30
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        acc = torch.empty((), dtype=torch.float32, device=dev)
+        stream = torch.cuda.current_stream(dev)
+        res = {}
+        for name, f, moved in (("copy_read_plus_write", lambda: dst.copy_(src), 2 * n),
+                               ("sum_read_only", lambda: torch.sum(src, dim=0, out=acc), n)):
+            ramp(f, args.ramp_ms)
+            t, _ = time_launches(f, 20, stream)
+            res[name] = {"avg_us": round(t * 1e6, 2), "bytes": moved,
+                         "gbs": round(moved / t / 1e9, 1),
+                         "frac_of_8tbs": round(moved / t / 1e9 / HBM_PEAK_GBS, 4)}
+        print(json.dumps({"hbm_ceiling": res}), flush=True)
         return
 
     print("bench: drawing workload %s" % args.config, file=sys.stderr, flush=True)

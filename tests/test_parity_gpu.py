@@ -460,9 +460,11 @@ def test_gather_grouped_output(gg, bm):
     _gather_case(gg, n_tokens=97, E=5, K=136, N=264, topk=3, seed=42, bm=bm, use_dst=False)
 
 
-def test_gather_out_of_range_indices(gg):
+@pytest.mark.parametrize("bm", [0, 32, 256])
+def test_gather_out_of_range_indices(gg, bm):
     # source indices outside [0, n_src) read zeros; destinations outside
-    # [0, M_cap) are not written; rows past off[E] are never touched
+    # [0, M_cap) are not written; rows past off[E] are never touched (at each
+    # height the destinations are read before the tile's last slice)
     rng = np.random.default_rng(43)
     E, K, N, n_src = 3, 72, 264, 40
     sizes = [10, 0, 20]
@@ -474,12 +476,12 @@ def test_gather_out_of_range_indices(gg):
     dst[[3, 20]] = [36, -1]
     dev = torch.device("cuda:0")
     C = torch.full((36, N), float("nan"), dtype=torch.float32, device=dev)
-    _say("case gather out-of-range")
+    _say("case gather out-of-range bm=%d" % bm)
     gg.grouped_gemm_gather(torch.from_numpy(X.view(np.int16)).to(dev).view(torch.bfloat16),
                            torch.from_numpy(src).to(dev),
                            torch.from_numpy(w.B.view(np.int16)).to(dev).view(torch.bfloat16),
                            torch.from_numpy(w.offsets).to(dev), dst_rows=torch.from_numpy(dst).to(dev),
-                           out=C, bm=0)
+                           out=C, bm=bm)
     torch.cuda.synchronize()
     got = C.cpu().numpy()
     ref, s = oracle.grouped_gemm_indexed(X, src, w.B, w.offsets, dst, M_cap=36)

@@ -157,6 +157,33 @@ def cpu_baseline(w, budget_s=12.0):
     }
 
 
+def launch_counts(sizes, K, N, args):
+    """Useful flops, algorithmic bytes and the matrix-core peak of one launch.
+
+    Useful flops are 2 * M_tot * K * N. The bytes count what the method must
+    move, once: A's routed rows, B of every expert with rows, and C, each at
+    its own element size (fp8 operands with their fp32 scales). Padding,
+    repeated reads and empty experts' weights are not counted. Gathered rows
+    add their two index lists; the combine adds a read of each output element
+    and a weight per row."""
+    import numpy as np
+    sizes = np.asarray(sizes)
+    M_tot = int(sizes.sum())
+    useful = 2.0 * M_tot * K * N
+    c_bytes = {"fp32": 4, "bf16": 2, "swiglu": 1}[args.out]  # per product column
+    active = int((sizes > 0).sum())
+    b_bytes = 2 * K * N * active if args.weights == "bf16" else (K + 4) * N * active
+    a_bytes = 2 * M_tot * K if args.acts == "bf16" else (K + 4) * M_tot
+    alg_bytes = (a_bytes + b_bytes + c_bytes * M_tot * N
+                 + (8 * M_tot if args.gather else 0)
+                 # the combine reads each output element before adding, and a weight per row
+                 + (4 * M_tot * N + 4 * M_tot if args.combine else 0))
+    # the matrix-core peak of the operand type: fp8 x fp8 on the fp8 cores,
+    # otherwise bf16 (fp8 weights are widened to bf16 for the matrix cores)
+    mfma_peak = MFMA_FP8_PEAK_TFLOPS if args.acts == "fp8" else MFMA_BF16_PEAK_TFLOPS
+    return useful, alg_bytes, mfma_peak
+
+
 def prepare(w, args, dev):
     """Device inputs for one workload and the launch a step makes.
 
@@ -219,18 +246,7 @@ def prepare(w, args, dev):
         else:
             gg.grouped_gemm(A, B, off, out=C, bm=args.bm)
 
-    useful = 2.0 * w.M_tot * w.K * w.N
-    c_bytes = {"fp32": 4, "bf16": 2, "swiglu": 1}[args.out]  # per product column
-    active = int((w.sizes > 0).sum())
-    b_bytes = 2 * w.K * w.N * active if args.weights == "bf16" else (w.K + 4) * w.N * active
-    a_bytes = 2 * w.M_tot * w.K if args.acts == "bf16" else (w.K + 4) * w.M_tot
-    alg_bytes = (a_bytes + b_bytes + c_bytes * w.M_tot * w.N
-                 + (8 * w.M_tot if args.gather else 0)
-                 # the combine reads each output element before adding, and a weight per row
-                 + (4 * w.M_tot * w.N + 4 * w.M_tot if args.combine else 0))
-    # the matrix-core peak of the operand type: fp8 x fp8 on the fp8 cores,
-    # otherwise bf16 (fp8 weights are widened to bf16 for the matrix cores)
-    mfma_peak = MFMA_FP8_PEAK_TFLOPS if args.acts == "fp8" else MFMA_BF16_PEAK_TFLOPS
+    useful, alg_bytes, mfma_peak = launch_counts(w.sizes, w.K, w.N, args)
     return {"step": step, "useful": useful, "alg_bytes": alg_bytes, "mfma_peak": mfma_peak,
             "off": off, "A": A, "B": B, "C": C}
 

@@ -280,21 +280,36 @@ __device__ __forceinline__ void run_tile_q8(const TileArgs &t, lds_u16 *lds_base
   if constexpr (C::MI <= 4) {
     k_loop<C::AD, C::BD, 2>(KT, ops, epilogue);
   } else {
-    // the tallest tile's registers do not hold the scales through its last
-    // slice (it spilled): it loads them per block and stores after the loop
+    // The tallest tile's registers do not hold the scales through its last
+    // slice (it spilled), so it stores after the loop. Loading a scale per
+    // block there would wait on the stores already issued (one counter
+    // covers both), so the scales go through LDS, free once the loop's final
+    // barrier has passed: each thread loads one row or column scale.
+    // Measured against per-block loads (one box, outputs bitwise equal):
+    // uniform16k 86.0 -> 80.3 us, skew16k 124.8 -> 116.7 us.
+    static_assert(C::BM + C::BN <= kThreads, "one scale per thread");
     k_loop<C::AD, C::BD, 2>(KT, ops);
+    lds_f32 *const sc = (lds_f32 *)lds_base;  // [BM] row scales, then [BN] column scales
+    if (t.tid < C::BM) {
+      sc[t.tid] = t.tid < t.rows ? ld_g4f(t.a_scale + t.tid) : 0.f;
+    } else if (t.tid < C::BM + C::BN) {
+      const int n = t.tid - C::BM;
+      sc[C::BM + n] = n < t.ncols ? ld_g4f(t.scale + n) : 0.f;
+    }
+    __syncthreads();
 #pragma unroll
     for (int mi = 0; mi < C::MI; ++mi) {
       const int m = wm0 + mi * 16 + s;
       if (m < t.rows) {
-        const float sa = ld_g4f(t.a_scale + m);
+        const float sa = sc[m];
 #pragma unroll
         for (int ni = 0; ni < C::NI; ++ni) {
           const int n = wn0 + ni * 16 + 4 * g;
-          if (n < t.ncols) put(m, n, acc[ni][mi] * sa * ld_g16f(t.scale + n));
+          if (n < t.ncols) put(m, n, acc[ni][mi] * sa * *(const lds_f32x4 *)(sc + C::BM + n));
         }
       }
     }
+    __syncthreads();  // the next tile's first stage stores overwrite the scales
   }
 }
 

@@ -247,6 +247,36 @@ def test_fp8_sampled(gg, full):
     assert worst <= parity.FP8_TRIPWIRE, "%s: worst error / bound %.3e" % (full.name, worst)
 
 
+def test_fp8_whole(gg, full):
+    # Every output of the fp8 x fp8 product against the oracle. The bound is
+    # check_fp8's with each group's largest product replaced by the group's
+    # sum (G <= S): looser than the sampled check above, but over the whole
+    # output, so a wrong tile, row, column or scale anywhere fails it.
+    w = full.w
+    _say("case full fp8 x fp8 whole %s: quantizing" % full.name)
+    Aq, a_scale = wl.fp8_activations(w)
+    Bq, b_scale = wl.fp8_weights(w)
+    dev = torch.device("cuda:0")
+    big, C = _guarded(w.M_cap, w.N, torch.float32)
+    gg.grouped_gemm_fp8(torch.from_numpy(Aq).to(dev), torch.from_numpy(a_scale).to(dev),
+                        torch.from_numpy(Bq).to(dev), torch.from_numpy(b_scale).to(dev),
+                        full.off, out=C, bm=0)
+    torch.cuda.synchronize()
+    out = _host(big)
+    assert np.isnan(out[w.M_cap:]).all()
+    ref, S = oracle.grouped_gemm_fp8(Aq, a_scale, Bq, b_scale, w.offsets, M_cap=w.M_cap)
+    m = w.M_tot
+    assert np.isfinite(out[:m]).all()
+    bound = parity.fp8_bound(S[:m], S[:m], w.K)
+    ratio = np.abs(out[:m].astype(np.float64) - ref[:m]) / np.maximum(bound, 1e-300)
+    worst = float(ratio.max()) if ratio.size else 0.0
+    _say("  %s fp8 whole: worst error / loose bound %.3e" % (full.name, worst))
+    assert worst <= 1.0, "%s: %d outputs beyond the fp8 bound" % (full.name, int((ratio > 1).sum()))
+    # the loose bound is never below the tight one, so the tight check's
+    # tripwire holds here too wherever the tight one holds
+    assert worst <= parity.FP8_TRIPWIRE, "%s: worst error / loose bound %.3e" % (full.name, worst)
+
+
 @pytest.mark.parametrize("full", ["decode"], indirect=True)
 def test_gather_routed_top8_decode(gg, full):
     # the decode shape reached through routing: 64 tokens, top-8 over 32

@@ -272,6 +272,11 @@ def library_yardstick(w, run, args, stream):
         C3 = C[: w.M_tot].view(w.E, m, w.N)
         cases["bmm_strided_batched"] = lambda: torch.bmm(A3, B, out_dtype=torch.float32, out=C3)
     views = [(A[off[e]:off[e + 1]], B[e], C[off[e]:off[e + 1]]) for e in experts]
+    # the same flops as one dense product with a single expert's weights
+    # (M_tot x K times K x N): no weight stream, the library's best case
+    if experts:
+        A2, B2, C2 = A[: w.M_tot], B[experts[0]], C[: w.M_tot]
+        cases["dense_one_weight_matrix"] = lambda: torch.mm(A2, B2, out_dtype=torch.float32, out=C2)
 
     def loop():
         for a, b, c in views:

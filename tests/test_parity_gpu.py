@@ -834,6 +834,42 @@ def test_many_tiles_per_workgroup(gg, bm, K):
     _full_compare(gg, w, bm, "many-tiles K=%d" % K)
 
 
+# ---- seeded random shapes ----------------------------------------------------------------
+
+def _random_workload(seed):
+    # E in 1..96; K and N any multiple of 8 up to 1280 and 1200 (so the last
+    # K slice and column tile are usually partial); a fifth of the experts
+    # empty, most small, some of several hundred rows; spare rows past the
+    # last group; M_tot * K * N kept at or below 4e8 so the oracle is quick
+    rng = np.random.default_rng(1000 + seed)
+    E = int(rng.integers(1, 97))
+    K = 8 * int(rng.integers(1, 161))
+    N = 8 * int(rng.integers(1, 151))
+    kind = rng.random(E)
+    sizes = np.where(kind < 0.2, 0, np.where(kind < 0.8, rng.integers(1, 40, E),
+                                             rng.integers(40, 700, E)))
+    cap = 4e8 / (K * N)
+    if sizes.sum() > cap:
+        sizes = np.floor(sizes * (cap / sizes.sum())).astype(np.int64)
+    bm = BMS[int(rng.integers(len(BMS)))]
+    w = wl.make_workload(E=E, K=K, N=N, sizes=[int(x) for x in sizes], seed=2000 + seed,
+                         M_cap=int(sizes.sum()) + int(rng.integers(0, 40)))
+    return w, bm
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_shapes(gg, seed):
+    w, bm = _random_workload(seed)
+    _full_compare(gg, w, bm, "random seed %d" % seed)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_shapes_fp8w(gg, seed):
+    w, bm = _random_workload(seed)
+    Bq, scale = wl.fp8_weights(w)
+    _fp8_compare(gg, w, Bq, scale, bm, "random seed %d" % seed)
+
+
 # ---- capture in a HIP graph -------------------------------------------------------------
 
 def test_graph_capture_replays(gg):

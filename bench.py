@@ -398,8 +398,9 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (for counter calibration)")
     ap.add_argument("--hbm-ceiling", action="store_true",
-                    help="time only plain device-wide streams (a 1 GiB copy and a 1 GiB "
-                         "read-only reduction through torch) for the box's practical HBM rate")
+                    help="time only plain device-wide streams through torch (a 1 GiB copy, the "
+                         "sum of two 1 GiB buffers and a 1 GiB read-only reduction) for the "
+                         "box's practical HBM rate")
     ap.add_argument("--library-yardstick", action="store_true",
                     help="time only the same products through hipBLASLt (torch) beside this "
                          "library's launch (bf16 weights, fp32 output, grouped rows)")
@@ -442,11 +443,16 @@ def main():
     if args.hbm_ceiling:
         n = 1 << 30
         src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        src2 = torch.ones_like(src)
         dst = torch.empty_like(src)
         acc = torch.empty((), dtype=torch.float32, device=dev)
         stream = torch.cuda.current_stream(dev)
         res = {}
+        # the sum of two buffers reads two bytes per byte written, near the
+        # grouped product's own mix at fp32 output (about 69% of its bytes read)
         for name, f, moved in (("copy_read_plus_write", lambda: dst.copy_(src), 2 * n),
+                               ("add_two_reads_one_write",
+                                lambda: torch.add(src, src2, out=dst), 3 * n),
                                ("sum_read_only", lambda: torch.sum(src, dim=0, out=acc), n)):
             ramp(f, args.ramp_ms)
             t, _ = time_launches(f, 20, stream)

@@ -6,9 +6,10 @@ benchmark times (bm=0, the device's per-expert tile height). The oracle
 computes the whole fp32 product once per workload; the fp32, bf16, SwiGLU,
 gather/scatter, weighted-combine and fp8-weight outputs are then compared
 element by element with it, each output followed by guard rows that must
-stay untouched. The fp8 x fp8 product is compared on sampled entries (its
-error bound needs the per-group largest product, computed one entry at a
-time).
+stay untouched. The fp8 x fp8 product gets an oracle of its own, also once
+per workload: its fp32 output is compared on sampled entries at its tight
+bound (which needs each group's largest product, computed one entry at a
+time) and whole at a looser one, and its bf16 and SwiGLU outputs whole.
 
 The workload fixture is module-scoped and parametrized, so pytest runs all
 tests of one workload before drawing the next.
@@ -220,17 +221,49 @@ def _samples(w, rng, n_random=3000):
     return np.array(rows, dtype=np.int64), np.array(cols, dtype=np.int64)
 
 
-def test_fp8_sampled(gg, full):
+@dataclasses.dataclass
+class Q8:
+    Aq: np.ndarray      # host codes and scales
+    a_scale: np.ndarray
+    Bq: np.ndarray
+    b_scale: np.ndarray
+    dev: list           # the same four on the device
+    ref: np.ndarray     # oracle C, float64 [M_tot, N]
+    S: np.ndarray       # oracle sum |products|, float64 [M_tot, N]
+    loose: np.ndarray   # the fp8 bound with each group's largest product replaced by its sum
+
+
+@pytest.fixture(scope="module")
+def q8(full):
+    # the fp8 x fp8 inputs of a workload and the oracle's whole product, once
     w = full.w
-    _say("case full fp8 x fp8 %s: quantizing" % full.name)
+    _say("fp8 x fp8 %s: quantizing" % full.name)
     Aq, a_scale = wl.fp8_activations(w)
     Bq, b_scale = wl.fp8_weights(w)
+    _say("oracle: whole fp8 x fp8 %s product" % full.name)
+    ref, S = oracle.grouped_gemm_fp8(Aq, a_scale, Bq, b_scale, w.offsets, M_cap=w.M_cap)
+    m = w.M_tot
     dev = torch.device("cuda:0")
-    big, C = _guarded(w.M_cap, w.N, torch.float32)
-    gg.grouped_gemm_fp8(torch.from_numpy(Aq).to(dev), torch.from_numpy(a_scale).to(dev),
-                        torch.from_numpy(Bq).to(dev), torch.from_numpy(b_scale).to(dev),
-                        full.off, out=C, bm=0)
+    d = [torch.from_numpy(x).to(dev) for x in (Aq, a_scale, Bq, b_scale)]
+    # G <= S for every group, so this bound is never below the tight one
+    q = Q8(Aq, a_scale, Bq, b_scale, d, ref[:m], S[:m], parity.fp8_bound(S[:m], S[:m], w.K))
+    yield q
+    del q, d
+    torch.cuda.empty_cache()
+
+
+def _fp8_run(gg, full, q8, out, swiglu=False):
+    f = gg.grouped_gemm_fp8_swiglu if swiglu else gg.grouped_gemm_fp8
+    f(*q8.dev, full.off, out=out, bm=0)
     torch.cuda.synchronize()
+
+
+def test_fp8_sampled(gg, full, q8):
+    w = full.w
+    Aq, a_scale, Bq, b_scale = q8.Aq, q8.a_scale, q8.Bq, q8.b_scale
+    _say("case full fp8 x fp8 %s" % full.name)
+    big, C = _guarded(w.M_cap, w.N, torch.float32)
+    _fp8_run(gg, full, q8, C)
     out = _host(big)
     assert np.isfinite(out[: w.M_tot]).all()
     assert np.isnan(out[w.M_cap:]).all()
@@ -247,34 +280,73 @@ def test_fp8_sampled(gg, full):
     assert worst <= parity.FP8_TRIPWIRE, "%s: worst error / bound %.3e" % (full.name, worst)
 
 
-def test_fp8_whole(gg, full):
+def test_fp8_whole(gg, full, q8):
     # Every output of the fp8 x fp8 product against the oracle. The bound is
     # check_fp8's with each group's largest product replaced by the group's
     # sum (G <= S): looser than the sampled check above, but over the whole
     # output, so a wrong tile, row, column or scale anywhere fails it.
     w = full.w
-    _say("case full fp8 x fp8 whole %s: quantizing" % full.name)
-    Aq, a_scale = wl.fp8_activations(w)
-    Bq, b_scale = wl.fp8_weights(w)
-    dev = torch.device("cuda:0")
+    _say("case full fp8 x fp8 whole %s" % full.name)
     big, C = _guarded(w.M_cap, w.N, torch.float32)
-    gg.grouped_gemm_fp8(torch.from_numpy(Aq).to(dev), torch.from_numpy(a_scale).to(dev),
-                        torch.from_numpy(Bq).to(dev), torch.from_numpy(b_scale).to(dev),
-                        full.off, out=C, bm=0)
-    torch.cuda.synchronize()
+    _fp8_run(gg, full, q8, C)
     out = _host(big)
     assert np.isnan(out[w.M_cap:]).all()
-    ref, S = oracle.grouped_gemm_fp8(Aq, a_scale, Bq, b_scale, w.offsets, M_cap=w.M_cap)
     m = w.M_tot
     assert np.isfinite(out[:m]).all()
-    bound = parity.fp8_bound(S[:m], S[:m], w.K)
-    ratio = np.abs(out[:m].astype(np.float64) - ref[:m]) / np.maximum(bound, 1e-300)
+    ratio = np.abs(out[:m] - q8.ref) / np.maximum(q8.loose, 1e-300)
     worst = float(ratio.max()) if ratio.size else 0.0
     _say("  %s fp8 whole: worst error / loose bound %.3e" % (full.name, worst))
     assert worst <= 1.0, "%s: %d outputs beyond the fp8 bound" % (full.name, int((ratio > 1).sum()))
     # the loose bound is never below the tight one, so the tight check's
     # tripwire holds here too wherever the tight one holds
     assert worst <= parity.FP8_TRIPWIRE, "%s: worst error / loose bound %.3e" % (full.name, worst)
+
+
+def test_fp8_bf16_out_whole(gg, full, q8):
+    # bf16 C of the fp8 x fp8 product: bit for bit the fp32 entry point's
+    # output rounded by torch, and inside the bf16 roundings of the oracle's
+    # value -/+ the loose fp8 bound, everywhere
+    w = full.w
+    m = w.M_tot
+    _say("case full fp8 x fp8 bf16-out %s" % full.name)
+    big, C = _guarded(w.M_cap, w.N, torch.bfloat16)
+    _fp8_run(gg, full, q8, C)
+    c32 = torch.empty((w.M_cap, w.N), dtype=torch.float32, device="cuda:0")
+    _fp8_run(gg, full, q8, c32)
+    assert torch.equal(c32[:m].to(torch.bfloat16).view(torch.int16), C[:m].view(torch.int16))
+    out = _host(big)
+    assert np.isnan(out[m:]).all()
+    step = 2048  # brackets built in row blocks to bound the host memory they need
+    for r0 in range(0, m, step):
+        r1 = min(m, r0 + step)
+        parity.check_fp8_bf16(out[r0:r1], q8.ref[r0:r1], q8.S[r0:r1], q8.S[r0:r1], w.K,
+                              "%s fp8 bf16-out rows %d..%d" % (full.name, r0, r1))
+
+
+def test_fp8_swiglu_whole(gg, full, q8):
+    # SwiGLU of the fp8 x fp8 gate/up product: bracketed by silu's range over
+    # the loose fp8 bound around the oracle's product, and equal to the SwiGLU
+    # of the fp32 entry point's output within the fp32 evaluation error
+    w = full.w
+    m = w.M_tot
+    _say("case full fp8 x fp8 swiglu %s" % full.name)
+    big, H = _guarded(w.M_cap, w.N // 2, torch.bfloat16)
+    _fp8_run(gg, full, q8, H, swiglu=True)
+    c32 = torch.empty((w.M_cap, w.N), dtype=torch.float32, device="cuda:0")
+    _fp8_run(gg, full, q8, c32)
+    out = _host(big)
+    c64 = _host(c32[:m])
+    assert np.isnan(out[m:]).all()
+    step = 2048
+    for r0 in range(0, m, step):
+        r1 = min(m, r0 + step)
+        what = "%s fp8 swiglu rows %d..%d" % (full.name, r0, r1)
+        parity.check_swiglu_bf16(out[r0:r1], q8.ref[r0:r1], q8.S[r0:r1], what,
+                                 err=q8.loose[r0:r1])
+        h64 = oracle.swiglu_pairs(c64[r0:r1])
+        slack = parity.swiglu_eval_slack(c64[r0:r1], h64)
+        assert (out[r0:r1] >= oracle.round_to_bf16(h64 - slack)).all(), what
+        assert (out[r0:r1] <= oracle.round_to_bf16(h64 + slack)).all(), what
 
 
 @pytest.mark.parametrize("full", ["decode"], indirect=True)

@@ -67,13 +67,16 @@ DESCRIPTIONS = {
 
 def kernel_source_hash():
     """Hash of the kernel sources with comments and blank space taken out, so
-    that a change to a comment does not mark the measured counters stale."""
+    that a change to a comment does not mark the measured counters stale. The
+    blocks only the tracing build compiles (#ifdef GG_TILE_TRACE) are taken
+    out too: the product library is built without them."""
     import re
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "moe_ragged_grouped_amd", "csrc")
     for fn in sorted(os.listdir(csrc)):
         with open(os.path.join(csrc, fn), encoding="utf-8") as f:
             text = f.read()
+        text = re.sub(r"#ifdef GG_TILE_TRACE\b.*?#endif", " ", text, flags=re.S)
         text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
         text = re.sub(r"//[^\n]*", " ", text)
         h.update(fn.encode())
@@ -320,6 +323,78 @@ def library_yardstick(w, run, args, stream):
     return out
 
 
+def tile_trace_summary(tr, khz, wg_total, n_tiles):
+    """Summary of one traced launch (gg_trace_grouped_gemm_bf16's records):
+    times in microseconds from the earliest workgroup start."""
+    import numpy as np
+    import moe_ragged_grouped_amd as gg
+    us = 1000.0 / khz
+    W = gg.TRACE_WORKGROUPS
+    wg = tr[:wg_total]
+    tl = tr[W:W + n_tiles]
+    assert (tl[:, 0] > 0).all() and (tl[:, 2] >= tl[:, 1]).all() and \
+        (tl[:, 1] >= tl[:, 0]).all(), "a tile has no record"
+    assert int(wg[:, 3].sum()) == n_tiles, "the workgroups ran %d of %d tiles" % (
+        int(wg[:, 3].sum()), n_tiles)
+    t0 = int(wg[:, 0].min())
+    start = (tl[:, 0] - t0) * us
+    decoded = (tl[:, 1] - t0) * us
+    end = (tl[:, 2] - t0) * us
+    dur = end - start
+    height = tl[:, 3]
+    owner = tl[:, 4]
+    finish = np.zeros(wg_total)
+    busy = np.zeros(wg_total)
+    np.maximum.at(finish, owner, end)
+    np.add.at(busy, owner, dur)
+    gaps = []
+    for b in range(wg_total):
+        s_b = np.sort(start[owner == b])
+        e_b = np.sort(end[owner == b])
+        if len(s_b) > 1:
+            gaps.extend((s_b[1:] - e_b[:-1]).tolist())
+    xcc = (wg[:, 2] >> 6).astype(int)
+    first = np.full(wg_total, np.inf)
+    np.minimum.at(first, owner, start)
+    entry = (wg[:, 0] - t0) * us
+    out = {
+        "span_us": round(float(end.max()), 2),
+        "entry_to_first_tile_us": round(float(np.mean(first[np.isfinite(first)] -
+                                                      entry[np.isfinite(first)])), 2),
+        "schedule_build_us": round(float(np.mean((wg[:, 1] - wg[:, 0]) * us)), 2),
+        "workgroup_finish_us": {"min": round(float(finish.min()), 1),
+                                "mean": round(float(finish.mean()), 1),
+                                "max": round(float(finish.max()), 1)},
+        "workgroup_busy_us": {"mean": round(float(busy.mean()), 1),
+                              "max": round(float(busy.max()), 1)},
+        "gap_between_tiles_us": ({"median": round(float(np.median(gaps)), 2),
+                                  "p90": round(float(np.percentile(gaps, 90)), 2),
+                                  "count": len(gaps)} if gaps else None),
+        "tile_decode_us": {"median": round(float(np.median(decoded - start)), 2),
+                           "p90": round(float(np.percentile(decoded - start, 90)), 2)},
+        "tiles_by_height": {int(h): {"count": int((height == h).sum()),
+                                     "mean_us": round(float(dur[height == h].mean()), 1)}
+                            for h in sorted(set(height.tolist()))},
+        "xcd_busy_mean_us": [round(float(busy[xcc == x].mean()), 1) if (xcc == x).any() else None
+                             for x in range(8)],
+        # the launch order assumes workgroup b runs on XCD b % 8
+        "workgroups_on_xcd_b_mod_8": round(float(np.mean(xcc == np.arange(wg_total) % 8)), 4),
+    }
+    # the tallest tiles by when they start: early (first 30% of the span)
+    # against late (after 60%)
+    tall = height == height.max()
+    early, late = tall & (start < 0.3 * end.max()), tall & (start > 0.6 * end.max())
+    if early.any() and late.any():
+        out["tallest_tile_us_by_start"] = {"first_30pct": round(float(dur[early].mean()), 1),
+                                           "after_60pct": round(float(dur[late].mean()), 1)}
+    # mean duration per first column, where the launch has few column positions
+    col0 = tl[:, 7]
+    if len(set(col0.tolist())) <= 16:
+        out["tile_us_by_col0"] = {int(c): round(float(dur[col0 == c].mean()), 1)
+                                  for c in sorted(set(col0.tolist()))}
+    return out
+
+
 def ramp(step, ms):
     """Untimed launches for at least ms milliseconds; returns their count."""
     import torch
@@ -401,6 +476,10 @@ def main():
                     help="time only plain device-wide streams through torch (a 1 GiB copy, the "
                          "sum of two 1 GiB buffers and a 1 GiB read-only reduction) for the "
                          "box's practical HBM rate")
+    ap.add_argument("--tile-trace", action="store_true",
+                    help="time only the launch's per-tile timeline, through the tracing build "
+                         "(bf16 weights, fp32 C, grouped rows): workgroup finish times, tile "
+                         "durations by height, time per XCD")
     ap.add_argument("--library-yardstick", action="store_true",
                     help="time only the same products through hipBLASLt (torch) beside this "
                          "library's launch (bf16 weights, fp32 output, grouped rows)")
@@ -475,6 +554,37 @@ def main():
         print(json.dumps({"library_yardstick": library_yardstick(w, run, args, stream),
                           "workload": DESCRIPTIONS[args.config], "name": args.config,
                           "steps": args.steps, "warmup": args.warmup}), flush=True)
+        return
+    if args.tile_trace:
+        if args.weights != "bf16" or args.out != "fp32" or args.gather or args.acts != "bf16":
+            raise SystemExit("--tile-trace traces bf16 weights, fp32 C, grouped rows")
+        _, n_tiles = gg.tile_schedule(run["off"], w.N, w.M_cap, bm=args.bm)
+        shape = (gg.TRACE_WORKGROUPS + int(n_tiles), gg.TRACE_RECORD)
+        scratch = torch.zeros(shape, dtype=torch.int64, device=dev)
+        traces = [torch.zeros(shape, dtype=torch.int64, device=dev) for _ in range(3)]
+
+        def traced(buf):
+            return gg.traced_grouped_gemm(run["A"], run["B"], run["off"], n_tiles, out=run["C"],
+                                          bm=args.bm, trace=buf)[2]
+        traced(scratch)  # loads the tracing build's code before anything is timed
+        ramp(step, args.ramp_ms)
+        launch_s, _ = time_launches(step, args.steps, stream)
+        # A pause of the host leaves the next ~100 launches of the 16k shapes
+        # slow while the clocks recover, so the recorded launches come after
+        # a ramp of traced launches and 120 more without a wait.
+        ramp(lambda: traced(scratch), args.ramp_ms)
+        for _ in range(120):
+            khz = traced(scratch)
+        for buf in traces:
+            traced(buf)
+        torch.cuda.synchronize()
+        wg_total = int((traces[-1][:gg.TRACE_WORKGROUPS, 0] > 0).sum().item())
+        last = [tile_trace_summary(t.cpu().numpy(), khz, wg_total, int(n_tiles))
+                for t in traces]
+        print(json.dumps({"tile_trace": last, "workload": DESCRIPTIONS[args.config],
+                          "name": args.config, "workgroups": wg_total, "tiles": int(n_tiles),
+                          "clock_khz": khz, "product_launch_us": round(launch_s * 1e6, 2)}),
+              flush=True)
         return
     step()  # correctness launch position of the protocol
     # Clock ramp: after the seconds of host-side input generation the GPU sits

@@ -17,7 +17,9 @@ import os
 __all__ = ["grouped_gemm", "grouped_gemm_swiglu", "grouped_gemm_gather",
            "grouped_gemm_gather_combine", "grouped_gemm_fp8w", "grouped_gemm_fp8",
            "grouped_gemm_fp8_swiglu", "tile_schedule", "library_path", "load_library",
-           "GroupedGemmError", "BM_CHOICES", "TILE_N", "MAX_EXPERTS", "SYMBOLS"]
+           "traced_grouped_gemm", "trace_library_path", "load_trace_library",
+           "GroupedGemmError", "BM_CHOICES", "TILE_N", "MAX_EXPERTS", "SYMBOLS",
+           "TRACE_SYMBOLS", "TRACE_WORKGROUPS", "TRACE_RECORD"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libmoe_ragged_grouped_amd.so")
@@ -31,7 +33,14 @@ SYMBOLS = ("gg_grouped_gemm_bf16", "gg_grouped_gemm_bf16_bf16out", "gg_grouped_g
            "gg_grouped_gemm_fp8w", "gg_grouped_gemm_fp8", "gg_grouped_gemm_fp8_bf16out",
            "gg_grouped_gemm_fp8_swiglu", "gg_tile_schedule", "gg_status_string")
 
+# the tracing build (include/grouped_gemm_trace.h): a diagnostic library
+_TRACE_LIB_PATH = os.path.join(_HERE, "libmoe_ragged_grouped_amd_trace.so")
+TRACE_SYMBOLS = ("gg_trace_grouped_gemm_bf16", "gg_trace_clock_khz")
+TRACE_WORKGROUPS = 1024
+TRACE_RECORD = 8  # uint64 values per record
+
 _lib = None
+_trace_lib = None
 
 
 class GroupedGemmError(RuntimeError):
@@ -381,3 +390,64 @@ def tile_schedule(offsets, N: int, M_cap: int, bm: int = 0, max_tiles: int = Non
     _check(st, "gg_tile_schedule")
     count = int(n.item())
     return tiles[:min(count, max_tiles)], count
+
+
+def trace_library_path() -> str:
+    return _TRACE_LIB_PATH
+
+
+def load_trace_library():
+    """Load the tracing build (raises if it has not been built)."""
+    global _trace_lib
+    if _trace_lib is None:
+        if not os.path.exists(_TRACE_LIB_PATH):
+            raise GroupedGemmError(
+                "HIP library %s is not built; run `python -m moe_ragged_grouped_amd.build`"
+                % _TRACE_LIB_PATH)
+        lib = ctypes.CDLL(_TRACE_LIB_PATH)
+        vp, i32 = ctypes.c_void_p, ctypes.c_int32
+        lib.gg_trace_grouped_gemm_bf16.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, vp,
+                                                   i32, vp]
+        lib.gg_trace_grouped_gemm_bf16.restype = ctypes.c_int
+        lib.gg_trace_clock_khz.argtypes = [ctypes.POINTER(ctypes.c_int32)]
+        lib.gg_trace_clock_khz.restype = ctypes.c_int
+        lib.gg_status_string.argtypes = [ctypes.c_int]
+        lib.gg_status_string.restype = ctypes.c_char_p
+        _trace_lib = lib
+    return _trace_lib
+
+
+def traced_grouped_gemm(A, B, offsets, max_tiles: int, out=None, bm: int = 0, stream=None,
+                        trace=None):
+    """grouped_gemm (fp32 C) through the tracing build, with its timeline.
+
+    Returns (C, trace, khz): trace is the uint64 record buffer of
+    gg_trace_grouped_gemm_bf16 as an int64 device tensor
+    [TRACE_WORKGROUPS + max_tiles, TRACE_RECORD], khz the rate of its
+    counter. A trace tensor passed in is written as it is (records the launch
+    does not write keep their values); otherwise a cleared one is allocated.
+    """
+    import torch
+    lib = load_trace_library()
+    E, K, N, M_cap = _grouped_args(A, B, offsets)
+    if out is None:
+        out = torch.empty((M_cap, N), dtype=torch.float32, device=A.device)
+    elif out.dtype != torch.float32 or tuple(out.shape) != (M_cap, N) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous fp32 [M_cap, N] tensor")
+    shape = (TRACE_WORKGROUPS + int(max_tiles), TRACE_RECORD)
+    if trace is None:
+        trace = torch.zeros(shape, dtype=torch.int64, device=A.device)
+    elif (trace.dtype != torch.int64 or tuple(trace.shape) != shape or not trace.is_contiguous()
+          or trace.device != A.device):
+        raise ValueError("trace must be a contiguous int64 [%d, %d] tensor on A's device" % shape)
+    st = lib.gg_trace_grouped_gemm_bf16(A.data_ptr(), B.data_ptr(), offsets.data_ptr(),
+                                        out.data_ptr(), E, K, N, M_cap, int(bm), trace.data_ptr(),
+                                        int(max_tiles), _stream_handle(A.device, stream))
+    if st != 0:
+        raise GroupedGemmError("gg_trace_grouped_gemm_bf16: status %d (%s)"
+                               % (st, lib.gg_status_string(st).decode()))
+    khz = ctypes.c_int32(0)
+    st = lib.gg_trace_clock_khz(ctypes.byref(khz))
+    if st != 0:
+        raise GroupedGemmError("gg_trace_clock_khz: status %d" % st)
+    return out, trace, int(khz.value)

@@ -1,8 +1,11 @@
-"""Compile the gfx950 HIP library in-tree with hipcc.
+"""Compile the gfx950 HIP libraries in-tree with hipcc.
 
     python -m moe_ragged_grouped_amd.build
 
-produces moe_ragged_grouped_amd/libmoe_ragged_grouped_amd.so from csrc/.
+produces moe_ragged_grouped_amd/libmoe_ragged_grouped_amd.so from csrc/, and
+libmoe_ragged_grouped_amd_trace.so, the same sources built with GG_TILE_TRACE
+(the per-tile timeline of include/grouped_gemm_trace.h; a diagnostic the
+product library does not contain).
 """
 
 from __future__ import annotations
@@ -15,6 +18,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe_ragged_grouped_amd.so")
+TRACE_LIB = os.path.join(HERE, "libmoe_ragged_grouped_amd_trace.so")
 SOURCES = [os.path.join(CSRC, "grouped_gemm.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -31,8 +35,8 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False, extra=()) -> str:
-    tmp = LIB + ".tmp%d" % os.getpid()
+def build(verbose: bool = False, extra=(), out: str = LIB) -> str:
+    tmp = out + ".tmp%d" % os.getpid()
     cmd = [HIPCC, *FLAGS, *extra, "-o", tmp, *SOURCES]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -43,9 +47,14 @@ def build(verbose: bool = False, extra=()) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs))
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
+
+
+def build_trace(verbose: bool = False) -> str:
+    return build(verbose, extra=("-DGG_TILE_TRACE",), out=TRACE_LIB)
 
 
 if __name__ == "__main__":
     print(build(verbose=True, extra=sys.argv[1:]))
+    print(build_trace(verbose=True))

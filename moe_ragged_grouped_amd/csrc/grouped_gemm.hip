@@ -1,5 +1,8 @@
 // Ragged-M grouped GEMM for gfx950: kernels and the C-ABI entry points
-// declared in include/grouped_gemm.h.
+// declared in include/grouped_gemm.h. Built with GG_TILE_TRACE, the same
+// source also gives the tracing library of include/grouped_gemm_trace.h: the
+// blocks under that macro record a per-tile timeline, and the product
+// library is compiled without them.
 //
 // One persistent launch serves every expert. Each workgroup rebuilds the
 // tile-count prefix from the device-resident group offsets (gg_schedule.h),
@@ -17,6 +20,9 @@
 // tile) or its weight columns (same N tile) then meet in the same L2.
 
 #include "grouped_gemm.h"  // include/ (on the -I path)
+#ifdef GG_TILE_TRACE
+#include "grouped_gemm_trace.h"
+#endif
 #include "gg_common.h"
 #include "gg_mainloop.h"
 #include "gg_mainloop_q8.h"
@@ -56,7 +62,21 @@ struct Params {
   int n_dst;                // indexed form: rows of C (M_cap, or the combine's n_dst)
   const float *row_w;       // combine only: [M_cap] weight of each grouped row
   int tile_cap;             // upper bound of the tile count (check_sizes)
+#ifdef GG_TILE_TRACE
+  unsigned long long *trace;  // the tracing build's records (grouped_gemm_trace.h)
+  int trace_tiles;            // tiles with a record
+#endif
 };
+
+#ifdef GG_TILE_TRACE
+// The tracing build's clock: the constant-rate real-time counter, read with
+// every earlier scalar read complete so that the reading is not deferred.
+__device__ __forceinline__ unsigned long long trace_clock() {
+  const unsigned long long c = __builtin_amdgcn_s_memrealtime();
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  return c;
+}
+#endif
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
@@ -169,14 +189,28 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(Params p) {
   // empty asm keeps the compiler from rematerialising it in vector registers)
   uint32_t lds = (uint32_t)(uintptr_t)(lds_u16 *)lds_dyn;
   asm volatile("" : "+s"(lds));
+#ifdef GG_TILE_TRACE
+  const unsigned long long t_entry = trace_clock();
+#endif
   const int total = build_schedule(sched, p.off, p.E, p.M_cap, p.N, p.bm_fixed, p.tile_cap);
   const int G = gridDim.x;  // a multiple of kXcds
   const int b = blockIdx.x;
   const int slot = (b % kXcds) * (G / kXcds) + b / kXcds;
+#ifdef GG_TILE_TRACE
+  const unsigned long long t_built = trace_clock();
+  int n_run = 0;
+#endif
   for (int base = 0; base < total; base += G) {
     const int t = base + slot;
     if (t >= total) break;
+#ifdef GG_TILE_TRACE
+    __syncthreads();  // every wave has left the previous tile
+    const unsigned long long t_start = trace_clock();
+#endif
     const Tile tl = decode_tile(sched, p.off, t, p.E, p.M_cap, p.N, p.bm_fixed);
+#ifdef GG_TILE_TRACE
+    const unsigned long long t_decoded = trace_clock();
+#endif
     switch (tl.bm) {
       case 16:
         if constexpr (MASK & 1) {
@@ -193,7 +227,32 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(Params p) {
         if constexpr (MASK & 16) tile_call<Pick<P, Cfg256, Cfg256F, CfgQ256>, O, R>(p, tl, lds);
         break;
     }
+#ifdef GG_TILE_TRACE
+    // the tile's K loop ends with a workgroup barrier, so every wave is done
+    const unsigned long long t_end = trace_clock();
+    ++n_run;
+    if (threadIdx.x == 0 && t < p.trace_tiles) {
+      unsigned long long *r = p.trace + GG_TRACE_RECORD * (GG_TRACE_WORKGROUPS + (size_t)t);
+      r[0] = t_start;
+      r[1] = t_decoded;
+      r[2] = t_end;
+      r[3] = (unsigned long long)tl.bm;
+      r[4] = (unsigned long long)b;
+      r[5] = (unsigned long long)tl.expert;
+      r[6] = (unsigned long long)tl.rows;
+      r[7] = (unsigned long long)tl.col0;
+    }
+#endif
   }
+#ifdef GG_TILE_TRACE
+  if (threadIdx.x == 0 && b < GG_TRACE_WORKGROUPS) {
+    unsigned long long *r = p.trace + GG_TRACE_RECORD * (size_t)b;
+    r[0] = t_entry;
+    r[1] = t_built;
+    r[2] = __smid();  // XCC id << 6 | shader engine << 4 | CU
+    r[3] = (unsigned long long)n_run;
+  }
+#endif
 }
 
 __global__ __launch_bounds__(kThreads) void tile_schedule_kernel(const int32_t *off, int E, int N,
@@ -452,6 +511,30 @@ extern "C" gg_status_t gg_tile_schedule(const int32_t *group_offsets, int32_t E,
                      (int)bound, tiles, n_tiles, max_tiles);
   return hipGetLastError() == hipSuccess ? GG_OK : GG_ERR_LAUNCH;
 }
+
+#ifdef GG_TILE_TRACE
+extern "C" gg_status_t gg_trace_grouped_gemm_bf16(const void *A, const void *B,
+                                                  const int32_t *group_offsets, float *C,
+                                                  int32_t E, int32_t K, int32_t N, int32_t M_cap,
+                                                  int32_t bm, uint64_t *trace, int32_t max_tiles,
+                                                  void *stream) {
+  if (trace == nullptr || max_tiles < 0) return GG_ERR_INVALID_VALUE;
+  if (!aligned(trace, 8)) return GG_ERR_MISALIGNED;
+  Params p = make_params(A, B, group_offsets, C, E, K, N, M_cap, bm);
+  p.trace = reinterpret_cast<unsigned long long *>(trace);
+  p.trace_tiles = max_tiles;
+  return grouped_gemm<Out::F32, Rows::Grouped>(p, stream);
+}
+
+extern "C" gg_status_t gg_trace_clock_khz(int32_t *khz) {
+  if (khz == nullptr) return GG_ERR_INVALID_VALUE;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return GG_ERR_LAUNCH;
+  return hipDeviceGetAttribute(khz, hipDeviceAttributeWallClockRate, dev) == hipSuccess
+             ? GG_OK
+             : GG_ERR_LAUNCH;
+}
+#endif
 
 extern "C" const char *gg_status_string(gg_status_t status) {
   switch (status) {

@@ -17,10 +17,13 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER_DIR = os.path.join(ROOT, "include")
 
 
-def _declared_symbols():
+TRACE_HEADER = "grouped_gemm_trace.h"  # the tracing build's own entry points
+
+
+def _declared_symbols(trace=False):
     names = set()
     for fn in os.listdir(HEADER_DIR):
-        if fn.endswith(".h"):
+        if fn.endswith(".h") and (fn == TRACE_HEADER) == trace:
             text = open(os.path.join(HEADER_DIR, fn)).read()
             text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
             names.update(re.findall(r"\b(gg_[a-z0-9_]+)\s*\(", text))
@@ -35,11 +38,40 @@ def lib():
     return gg.load_library()
 
 
+@pytest.fixture(scope="module")
+def trace_lib():
+    if not os.path.exists(gg.trace_library_path()):
+        import moe_ragged_grouped_amd.build as b
+        b.build_trace()
+    return gg.load_trace_library()
+
+
 def test_exports_every_declared_symbol(lib):
     declared = _declared_symbols()
     assert declared == set(gg.SYMBOLS), declared
     for name in declared:
         assert hasattr(lib, name), name
+
+
+def test_tracing_build_exports_its_symbols(lib, trace_lib):
+    declared = _declared_symbols(trace=True)
+    assert declared == set(gg.TRACE_SYMBOLS), declared
+    for name in declared:
+        assert hasattr(trace_lib, name), name
+        assert not hasattr(lib, name), "the product library carries no tracing entry point"
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(trace=0), 1), (dict(max_tiles=-1), 1), (dict(trace=260), 2), (dict(A=0), 1),
+    (dict(E=0), 1), (dict(bm=48), 1), (dict(K=12), 2), (dict(E=1025), 3),
+])
+def test_trace_host_checks(trace_lib, kw, status):
+    a = dict(GOOD, trace=256, max_tiles=16)
+    a.update(kw)
+    assert trace_lib.gg_trace_grouped_gemm_bf16(a["A"], a["B"], a["off"], a["C"], a["E"], a["K"],
+                                                a["N"], a["M_cap"], a["bm"], a["trace"],
+                                                a["max_tiles"], None) == status
+    assert trace_lib.gg_trace_clock_khz(None) == 1
 
 
 def test_status_strings(lib):

@@ -480,6 +480,9 @@ def main():
                     help="time only the launch's per-tile timeline, through the tracing build "
                          "(bf16 weights, fp32 C, grouped rows): workgroup finish times, tile "
                          "durations by height, time per XCD")
+    ap.add_argument("--trace-out", default=None,
+                    help="with --tile-trace: also save the raw records of the three traced "
+                         "launches (int64 [3, records, values]) to this .npy file")
     ap.add_argument("--library-yardstick", action="store_true",
                     help="time only the same products through hipBLASLt (torch) beside this "
                          "library's launch (bf16 weights, fp32 output, grouped rows)")
@@ -578,6 +581,8 @@ def main():
         for buf in traces:
             traced(buf)
         torch.cuda.synchronize()
+        if args.trace_out:
+            np.save(args.trace_out, np.stack([t.cpu().numpy() for t in traces]))
         wg_total = int((traces[-1][:gg.TRACE_WORKGROUPS, 0] > 0).sum().item())
         last = [tile_trace_summary(t.cpu().numpy(), khz, wg_total, int(n_tiles))
                 for t in traces]

@@ -1,4 +1,5 @@
-"""bench.py's per-launch accounting, pinned to the figures written out by hand.
+"""bench.py's per-launch accounting, pinned to the figures written out by hand
+(and, last, its summary of a traced launch's timeline on a hand-made record set).
 
 The roofline fractions in every bench line divide these counts by the
 measured time, so each count is checked here against its parts:
@@ -98,3 +99,31 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode == 2
     assert "one GPU" in r.stderr
     assert r.stdout == ""
+
+
+def test_tile_trace_summary_of_a_known_timeline():
+    # two workgroups (XCDs 0 and 1), three tiles on a 100 MHz counter:
+    # workgroup 0 runs tiles 0 and 2, workgroup 1 tile 1
+    import moe_ragged_grouped_amd as gg
+    W, R = gg.TRACE_WORKGROUPS, gg.TRACE_RECORD
+    tr = np.zeros((W + 3, R), dtype=np.int64)
+    t0 = 10 ** 9
+    tr[0, :4] = [t0, t0 + 200, 0 << 6, 2]
+    tr[1, :4] = [t0 + 100, t0 + 300, 1 << 6, 1]
+    # start, decoded, end, bm, workgroup, expert, rows, col0 (ticks of 10 ns)
+    tr[W + 0] = [t0 + 250, t0 + 320, t0 + 4250, 256, 0, 0, 256, 0]
+    tr[W + 1] = [t0 + 350, t0 + 410, t0 + 2350, 64, 1, 1, 40, 0]
+    tr[W + 2] = [t0 + 4266, t0 + 4330, t0 + 8266, 256, 0, 2, 256, 256]
+    s = bench.tile_trace_summary(tr, 100000, 2, 3)
+    assert s["span_us"] == 82.66
+    assert s["workgroup_finish_us"] == {"min": 23.5, "mean": 53.1, "max": 82.7}
+    assert s["workgroup_busy_us"] == {"mean": 50.0, "max": 80.0}
+    assert s["gap_between_tiles_us"] == {"median": 0.16, "p90": 0.16, "count": 1}
+    assert s["schedule_build_us"] == 2.0
+    assert s["entry_to_first_tile_us"] == 2.5
+    assert s["tile_decode_us"]["median"] == 0.64
+    assert s["tiles_by_height"] == {64: {"count": 1, "mean_us": 20.0},
+                                    256: {"count": 2, "mean_us": 40.0}}
+    assert s["xcd_busy_mean_us"][:2] == [80.0, 20.0] and s["xcd_busy_mean_us"][2] is None
+    assert s["workgroups_on_xcd_b_mod_8"] == 1.0
+    assert s["tile_us_by_col0"] == {0: 30.0, 256: 40.0}

@@ -231,7 +231,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(Params p) {
     // the tile's K loop ends with a workgroup barrier, so every wave is done
     const unsigned long long t_end = trace_clock();
     ++n_run;
-    if (threadIdx.x == 0 && t < p.trace_tiles) {
+    if (threadIdx.x == 0 && p.trace != nullptr && t < p.trace_tiles) {
       unsigned long long *r = p.trace + GG_TRACE_RECORD * (GG_TRACE_WORKGROUPS + (size_t)t);
       r[0] = t_start;
       r[1] = t_decoded;
@@ -245,7 +245,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(Params p) {
 #endif
   }
 #ifdef GG_TILE_TRACE
-  if (threadIdx.x == 0 && b < GG_TRACE_WORKGROUPS) {
+  // the library's other entry points, also in the tracing build, pass no buffer
+  if (threadIdx.x == 0 && p.trace != nullptr && b < GG_TRACE_WORKGROUPS) {
     unsigned long long *r = p.trace + GG_TRACE_RECORD * (size_t)b;
     r[0] = t_entry;
     r[1] = t_built;

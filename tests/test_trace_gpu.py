@@ -64,3 +64,25 @@ def test_trace_matches_product_and_schedule(gg, bm):
         mine = rec[owner == b]
         assert (mine[1:, 0] >= mine[:-1, 2]).all(), "tiles of one workgroup overlap"
     assert tr.shape[1] == gg.TRACE_RECORD and (tr[W + n:] == 0).all()
+
+
+def test_tracing_build_runs_the_plain_entry_point(gg):
+    # the tracing library also exports the product's entry points; called
+    # without a trace buffer they record nothing and compute the same result
+    import ctypes
+    w = wl.make_workload(E=4, K=256, N=512, sizes=[100, 0, 37, 260], seed=62, M_cap=400)
+    A, B, off = _dev(w)
+    ref = gg.grouped_gemm(A, B, off, bm=0)
+    lib = gg.load_trace_library()
+    vp, i32 = ctypes.c_void_p, ctypes.c_int32
+    fn = lib.gg_grouped_gemm_bf16
+    fn.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
+    fn.restype = ctypes.c_int
+    C = torch.full_like(ref, float("nan"))
+    _say("case tracing build, plain entry point")
+    st = fn(A.data_ptr(), B.data_ptr(), off.data_ptr(), C.data_ptr(), w.E, w.K, w.N, w.M_cap, 0,
+            ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    torch.cuda.synchronize()
+    assert st == 0
+    m = w.M_tot
+    assert torch.equal(C[:m], ref[:m]) and torch.isnan(C[m:]).all()

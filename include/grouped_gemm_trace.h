@@ -9,9 +9,11 @@
  * workgroups of the persistent launch finish once tiles of different heights
  * share the machine.
  *
- * The traced kernel is the product kernel with one workgroup barrier and two
- * reads of the constant-rate real-time counter added per tile, so its tiles
- * run a little slower than the product's.
+ * The traced kernel is the product kernel with one workgroup barrier and
+ * three reads of the constant-rate real-time counter added per tile, so its
+ * tiles run a little slower than the product's. The tracing library also
+ * exports the entry points of grouped_gemm.h; they compute what the product
+ * library's do and record nothing.
  */
 #ifndef MOE_RAGGED_GROUPED_AMD_GROUPED_GEMM_TRACE_H
 #define MOE_RAGGED_GROUPED_AMD_GROUPED_GEMM_TRACE_H
